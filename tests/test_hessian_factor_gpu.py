@@ -1,0 +1,85 @@
+"""bakron_hessian and bakron_factor through the C ABI against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from two_sided_gptq_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bk():
+    from two_sided_gptq_amd import bakron
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    bakron.load()
+    return bakron
+
+
+@pytest.mark.parametrize("N,d", [(1, 1), (100, 65), (512, 64), (4096, 256), (333, 130)])
+def test_hessian_matches_oracle(bk, N, d):
+    g = np.random.default_rng(N * 1000 + d)
+    X = g.standard_normal((N, d)).astype(np.float32)
+    if d > 4:
+        X[:, 3] *= 20.0
+    H = bk.hessian(torch.from_numpy(X).cuda(), synth.DAMP)
+    torch.cuda.synchronize()
+    Hg = H.cpu().numpy().astype(np.float64)
+    Ho = oracle.hessian(X, synth.DAMP)
+    scale = np.sqrt(np.outer(np.diag(Ho), np.diag(Ho)))
+    err = np.max(np.abs(Hg - Ho) / scale)
+    assert err < 2e-5, err
+    assert np.allclose(Hg, Hg.T, rtol=0, atol=1e-6 * np.max(np.abs(Ho)))
+
+
+@pytest.mark.parametrize("d", [1, 7, 64, 65, 200, 512])
+def test_factor_matches_oracle(bk, d):
+    g = np.random.default_rng(d)
+    X = g.standard_normal((2 * d + 8, d)).astype(np.float32)
+    H = oracle.hessian(X, synth.DAMP).astype(np.float32)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L = bk.factor(torch.from_numpy(H).cuda(), dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    Lg = L.cpu().numpy().astype(np.float64)
+    Lo = oracle.factor(H.astype(np.float64))
+    assert np.array_equal(np.triu(Lg, 1), np.zeros_like(Lg))
+    assert np.all(np.diag(Lg) > 0)
+    # fp32 output of an fp64 computation: relative to the column scale of L
+    err = np.max(np.abs(Lg - Lo)) / np.max(np.abs(Lo))
+    assert err < 1e-6, err
+    R = Lg @ Lg.T @ H.astype(np.float64) - np.eye(d)
+    assert np.max(np.abs(R)) < 1e-3
+
+
+def test_factor_not_pd(bk):
+    H = -np.eye(70, dtype=np.float32)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bk.factor(torch.from_numpy(H).cuda(), dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & bk.DEV_NOT_PD
+
+
+def test_full_pipeline_c2(bk):
+    """GPU hessian -> GPU factor -> GPU quantize at 1024 x 1024; the result is
+    checked by the oracle's invariants (completion and rounding consistency)
+    on the factors the solver consumed."""
+    w = synth.WORKLOADS["c2a"]
+    W = synth.weights(w)
+    X = torch.from_numpy(synth.input_samples(w)).cuda()
+    Y = torch.from_numpy(synth.output_samples(w)).cuda()
+    LA = bk.factor(bk.hessian(X, synth.DAMP))
+    LB = bk.factor(bk.hessian(Y, synth.DAMP))
+    out = bk.quantize(torch.from_numpy(W).cuda(), LA, LB, kind=w.qkind, bits=w.qbits,
+                      want_E=True)
+    torch.cuda.synchronize()
+    LAh, LBh = LA.cpu().numpy(), LB.cpu().numpy()
+    V, E = out["V"].cpu().numpy(), out["E"].cpu().numpy()
+    codes, s = out["codes"].cpu().numpy(), out["scales"].cpu().numpy()
+    R = oracle.completion_residual(W, V, E, LAh, LBh)
+    assert np.max(np.abs(R)) < 1e-4 * float(np.max(s))
+    bad, ties = oracle.rounding_consistency(codes, V, E, np.diag(LAh), np.diag(LBh), s,
+                                            np.zeros_like(s), w.qkind, w.qbits)
+    assert bad == 0

@@ -1,0 +1,804 @@
+// quantize.hip -- bakron_quantize, the solver's hot path, for gfx950.
+//
+// Method: BaKron / FastKron (arXiv 2608.06291), as described on the
+// pith.science review page ("What carries the argument": Proposition 3.1,
+// anti-diagonal independence, band updates batched into two matrix products;
+// "Core claim": Theorem 3.2, O(m+n) sequential steps and O(mn(m+n)) work) and
+// the mlsanity.com index page (abstract).
+//
+// Pipeline for one call, all enqueued on the caller's stream:
+//   1. qparams    per-row scale / zero point from the original W
+//   2. relayout   W -> padded fp32 working copy Wp (mp x np, multiples of 64);
+//                 LA, LB -> padded lower-triangular copies (identity padding)
+//   3. schedule   in-order walk of the recursion over 64 x 64 TILE
+//                 anti-diagonals K = I + J (tiles on one tile anti-diagonal are
+//                 independent, for the same reason single entries on one
+//                 anti-diagonal are):
+//                   leaf(K)        one workgroup per tile, the whole in-tile
+//                                  problem solved in LDS, 127 diagonal steps
+//                   band(K, L, H)  postponed update from tile diagonals
+//                                  S = [K, K+H) to R = [K+H, K+L) as two
+//                                  staircase fp32-MFMA GEMMs
+//   4. finalise   sum of e^2 in a fixed order
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "common.hpp"
+
+namespace bakron {
+namespace {
+
+constexpr int TB = 64;  // tile edge (leaf tile and band-GEMM output tile)
+constexpr int LP = 68;  // LDS row stride in floats for the leaf tiles
+constexpr int GP = 68;  // LDS row stride in floats for the GEMM operand tiles
+constexpr int NPART = 1024;  // partial sums of the e^2 reduction
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ qparams
+// One workgroup per padded row.  Rows >= m get s = 1, z = 0 (the padding is
+// all zeros, so every padded entry rounds to its zero point exactly).
+__global__ __launch_bounds__(256) void qparams_kernel(
+    const float *__restrict__ W, int64_t m, int64_t n, int kind, int bits,
+    float *__restrict__ scales, float *__restrict__ zeros, float *__restrict__ sc_pad,
+    float *__restrict__ zp_pad, int32_t *dev_status) {
+    __shared__ float s_amax[256], s_lo[256], s_hi[256];
+    __shared__ int s_bad[256];
+    const int64_t i = blockIdx.x;
+    const int t = threadIdx.x;
+    float s = 1.0f, z = 0.0f;
+    if (i < m) {
+        float amax = 0.0f, lo = INFINITY, hi = -INFINITY;
+        int bad = 0;
+        const float *row = W + i * n;
+        for (int64_t j = t; j < n; j += 256) {
+            const float w = row[j];
+            bad |= !isfinite(w);
+            amax = fmaxf(amax, fabsf(w));
+            lo = fminf(lo, w);
+            hi = fmaxf(hi, w);
+        }
+        s_amax[t] = amax;
+        s_lo[t] = lo;
+        s_hi[t] = hi;
+        s_bad[t] = bad;
+        __syncthreads();
+        for (int off = 128; off > 0; off >>= 1) {
+            if (t < off) {
+                s_amax[t] = fmaxf(s_amax[t], s_amax[t + off]);
+                s_lo[t] = fminf(s_lo[t], s_lo[t + off]);
+                s_hi[t] = fmaxf(s_hi[t], s_hi[t + off]);
+                s_bad[t] |= s_bad[t + off];
+            }
+            __syncthreads();
+        }
+        if (kind == BAKRON_Q_SYM) {
+            s = s_amax[0] / (float)((1 << (bits - 1)) - 1);  // IEEE fp32 division
+            if (s == 0.0f) s = 1.0f;
+        } else if (kind == BAKRON_Q_ASYM) {
+            const float qmax = (float)((1 << bits) - 1);
+            const float range = s_hi[0] - s_lo[0];
+            s = range / qmax;
+            if (s == 0.0f) {
+                s = 1.0f;
+            } else {
+                z = fminf(fmaxf(rintf(-s_lo[0] / s), 0.0f), qmax);
+            }
+        }
+        if (t == 0) {
+            scales[i] = s;
+            if (zeros) zeros[i] = z;
+            if (s_bad[0] && dev_status) atomicOr(dev_status, BAKRON_DEV_NONFINITE);
+        }
+    }
+    if (t == 0) {
+        sc_pad[i] = s;
+        zp_pad[i] = z;
+    }
+}
+
+// ----------------------------------------------------------------- relayout
+// dst (prow x pcol, pcol % 4 == 0) from src (rows x cols).  tri = 0: plain
+// copy with zero padding.  tri = 1: lower triangle of a square factor, upper
+// part zero, padded diagonal one (so padded entries never divide by zero and
+// never couple to real ones).  Each thread writes one float4.
+__global__ __launch_bounds__(256) void relayout_kernel(
+    const float *__restrict__ src, int64_t rows, int64_t cols, float *__restrict__ dst,
+    int64_t prow, int64_t pcol, int tri, int vec_ok) {
+    const int64_t q4 = pcol / 4;
+    const int64_t total = prow * q4;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = idx / q4;
+        const int64_t c0 = (idx - r * q4) * 4;
+        float v[4];
+        if (r < rows && vec_ok && c0 + 3 < cols) {
+            const float4 x = *reinterpret_cast<const float4 *>(src + r * cols + c0);
+            v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[k] = (r < rows && c0 + k < cols) ? src[r * cols + c0 + k] : 0.0f;
+        }
+        if (tri) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t c = c0 + k;
+                if (r < rows && c < cols) {
+                    if (c > r) v[k] = 0.0f;
+                } else {
+                    v[k] = (c == r) ? 1.0f : 0.0f;
+                }
+            }
+        }
+        *reinterpret_cast<float4 *>(dst + r * pcol + c0) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
+// --------------------------------------------------------------------- leaf
+struct LeafArgs {
+    const float *Wp;  // mp x np working weights (all outside contributions applied)
+    float *Ebuf;      // order 1: E (mp x np); order 2: E^T (np x mp)
+    const float *LAp, *LBp;
+    const float *sc, *zp;
+    int64_t mp, np;
+    int M, N, order;
+    int qmin, qmax;
+    int8_t *codes;
+    float *V, *E;
+    int64_t m, n;
+    int32_t *dev_status;
+};
+
+// sum over the 8 consecutive lanes of a group (all 8 end with the total)
+__device__ inline float group8_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    return x;
+}
+
+__device__ inline float dot8(const float4 a0, const float4 a1, const float4 b0, const float4 b1) {
+    float s = a0.x * b0.x;
+    s = fmaf(a0.y, b0.y, s);
+    s = fmaf(a0.z, b0.z, s);
+    s = fmaf(a0.w, b0.w, s);
+    s = fmaf(a1.x, b1.x, s);
+    s = fmaf(a1.y, b1.y, s);
+    s = fmaf(a1.z, b1.z, s);
+    s = fmaf(a1.w, b1.w, s);
+    return s;
+}
+
+// The in-tile problem is the same two-sided rounding on a 64 x 64 block with
+// the diagonal blocks LB[I,I], LA[J,J].  It is solved in the order-free form
+// (each entry's value before rounding is W minus the contributions of every
+// entry before it in the product order):
+//   Z[r][c] = sum_{c' <= c} E[r][c'] LA[c][c']          (row direction)
+//   P[r][c] = W[r][c] - LB[r][r] sum_{c' < c} E[r][c'] LA[c][c']
+//                     - sum_{r' < r} LB[r][r'] Z[r'][c]  (column direction)
+// Step d rounds the in-tile anti-diagonal r + c = d; each of its entries is
+// handled by 8 lanes (two length-64 dot products split 8 ways, then a DPP
+// reduction).  E and Z start at zero, so the dots run over full rows and the
+// not-yet-computed terms contribute exact zeros.
+__global__ __launch_bounds__(512) void leaf_kernel(LeafArgs a, int K) {
+    __shared__ __align__(16) float Ws[TB * LP];
+    __shared__ __align__(16) float Es[TB * LP];
+    __shared__ __align__(16) float Zs[TB * LP];  // Zs[c][r] = Z[r][c]
+    __shared__ __align__(16) float Bs[TB * LP];  // LB[I,I]
+    __shared__ __align__(16) float As[TB * LP];  // LA[J,J]
+    __shared__ float s_sc[TB], s_isc[TB], s_zp[TB], s_ib[TB], s_ia[TB];
+    __shared__ int8_t Cs[TB * TB];
+
+    const int tid = threadIdx.x;
+    const int Ilo = max(0, K - a.N + 1);
+    const int I = Ilo + blockIdx.x;
+    const int J = K - I;
+    const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
+
+    for (int idx = tid; idx < TB * 16; idx += 512) {
+        const int r = idx >> 4, c4 = (idx & 15) * 4;
+        *reinterpret_cast<float4 *>(Ws + r * LP + c4) =
+            *reinterpret_cast<const float4 *>(a.Wp + (r0 + r) * a.np + c0 + c4);
+        *reinterpret_cast<float4 *>(Bs + r * LP + c4) =
+            *reinterpret_cast<const float4 *>(a.LBp + (r0 + r) * a.mp + r0 + c4);
+        *reinterpret_cast<float4 *>(As + r * LP + c4) =
+            *reinterpret_cast<const float4 *>(a.LAp + (c0 + r) * a.np + c0 + c4);
+        *reinterpret_cast<float4 *>(Es + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(Zs + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < TB) {
+        const float s = a.sc[r0 + tid];
+        s_sc[tid] = s;
+        s_isc[tid] = 1.0f / s;
+        s_zp[tid] = a.zp[r0 + tid];
+    }
+    __syncthreads();
+    if (tid < TB) {
+        s_ib[tid] = 1.0f / Bs[tid * LP + tid];
+        s_ia[tid] = 1.0f / As[tid * LP + tid];
+    }
+    __syncthreads();
+
+    const int g = tid >> 3, q = tid & 7;
+    const float qminf = (float)a.qmin, qmaxf = (float)a.qmax;
+    int bad = 0;
+    for (int d = 0; d < 2 * TB - 1; ++d) {
+        const int rlo = d < TB ? 0 : d - TB + 1;
+        const int rhi = d < TB ? d : TB - 1;
+        const int r = min(rlo + g, rhi);
+        const bool act = (rlo + g) <= rhi;
+        const int c = d - r;
+        const float4 *e4 = reinterpret_cast<const float4 *>(Es + r * LP);
+        const float4 *a4 = reinterpret_cast<const float4 *>(As + c * LP);
+        const float4 *b4 = reinterpret_cast<const float4 *>(Bs + r * LP);
+        const float4 *z4 = reinterpret_cast<const float4 *>(Zs + c * LP);
+        float d1 = dot8(e4[q], e4[8 + q], a4[q], a4[8 + q]);
+        float d2 = dot8(b4[q], b4[8 + q], z4[q], z4[8 + q]);
+        d1 = group8_sum(d1);
+        d2 = group8_sum(d2);
+        if (act && q == 0) {
+            const float P = Ws[r * LP + c] - Bs[r * LP + r] * d1 - d2;
+            const float u = P * s_isc[r];
+            const float cz = fminf(fmaxf(rintf(u) + s_zp[r], qminf), qmaxf);
+            const float v = s_sc[r] * (cz - s_zp[r]);
+            const float e = (P - v) * (s_ib[r] * s_ia[c]);
+            bad |= !isfinite(e);
+            Es[r * LP + c] = e;
+            Zs[c * LP + r] = fmaf(e, As[c * LP + c], d1);
+            Cs[r * TB + c] = (int8_t)(int)cz;
+        }
+        __syncthreads();
+    }
+
+    // E tile to the band-update buffer
+    if (a.order == BAKRON_ORDER_LA_FIRST) {
+        for (int idx = tid; idx < TB * 16; idx += 512) {
+            const int r = idx >> 4, c4 = (idx & 15) * 4;
+            *reinterpret_cast<float4 *>(a.Ebuf + (r0 + r) * a.np + c0 + c4) =
+                *reinterpret_cast<const float4 *>(Es + r * LP + c4);
+        }
+    } else {
+        for (int idx = tid; idx < TB * 16; idx += 512) {
+            const int c = idx >> 4, rr4 = (idx & 15) * 4;
+            *reinterpret_cast<float4 *>(a.Ebuf + (c0 + c) * a.mp + r0 + rr4) =
+                make_float4(Es[(rr4 + 0) * LP + c], Es[(rr4 + 1) * LP + c],
+                            Es[(rr4 + 2) * LP + c], Es[(rr4 + 3) * LP + c]);
+        }
+    }
+    // caller-visible outputs
+    for (int idx = tid; idx < TB * TB; idx += 512) {
+        const int r = idx >> 6, c = idx & 63;
+        const int64_t gi = r0 + r, gj = c0 + c;
+        if (gi < a.m && gj < a.n) {
+            const int8_t code = Cs[r * TB + c];
+            a.codes[gi * a.n + gj] = code;
+            if (a.V) a.V[gi * a.n + gj] = s_sc[r] * ((float)code - s_zp[r]);
+            if (a.E) a.E[gi * a.n + gj] = Es[r * LP + c];
+        }
+    }
+    if (bad && a.dev_status) atomicOr(a.dev_status, BAKRON_DEV_NONFINITE);
+}
+
+// -------------------------------------------------------------- band GEMMs
+// C[ci][cj] (=|-=) sum_{kb=klo..khi} A[ci-block][kb-block] . B[cj-block][kb-block]^T
+// on 64 x 64 tiles; both operands row-major with the contraction index
+// contiguous.  The tile indices and the staircase K range of each output tile
+// come from the recursion node (K, L, H):
+//   mode 0  (LA first, product 1)  Tt(J',I) = sum_J LA(J',J) E(I,J)^T
+//   mode 1  (LA first, product 2)  W(I',J') -= sum_I LB(I',I) Tt(J',I)^T
+//   mode 2  (LB first, product 1)  S(I',J) = sum_I LB(I',I) Et(J,I)^T
+//   mode 3  (LB first, product 2)  W(I',J') -= sum_J S(I',J) LA(J',J)^T
+// Grid: x = offset along the band, y = row index (from rlo).
+struct BandArgs {
+    const float *A, *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int mode, K, L, H, M, N, rlo, subtract;
+};
+
+__device__ inline bool band_tile(const BandArgs &g, int bx, int by, int &ci, int &cj,
+                                 int &klo, int &khi) {
+    const int K = g.K, H = g.H, row = g.rlo + by, o = bx;
+    if (g.mode == 0) {
+        const int I = row, Jp = K - I + o;
+        if (Jp < 0 || Jp >= g.N) return false;
+        ci = Jp; cj = I; klo = max(0, K - I); khi = min(Jp, K + H - 1 - I);
+    } else if (g.mode == 1) {
+        const int Ip = row, Jp = K + H + o - Ip;
+        if (Jp < 0 || Jp >= g.N) return false;
+        ci = Ip; cj = Jp; klo = max(0, K - Jp); khi = min(Ip, K + H - 1);
+    } else if (g.mode == 2) {
+        const int J = row, Ip = K - J + o;
+        if (Ip < 0 || Ip >= g.M) return false;
+        ci = Ip; cj = J; klo = max(0, K - J); khi = min(Ip, K + H - 1 - J);
+    } else {
+        const int Ip = row, Jp = K + H + o - Ip;
+        if (Jp < 0 || Jp >= g.N) return false;
+        ci = Ip; cj = Jp; klo = max(0, K - Ip); khi = min(Jp, K + H - 1);
+    }
+    return klo <= khi;
+}
+
+// 256 threads = 4 waves; wave w owns the 32 x 32 quadrant (w/2, w%2) of the
+// output tile and runs v_mfma_f32_32x32x2_f32.  Lane l supplies row l%32 of
+// its A quadrant and row l%32 of its B quadrant; the two k slots of each
+// instruction are k and k+32 of the 64-wide block (lanes 0-31 take the lower
+// half, lanes 32-63 the upper), so every lane reads its operands as
+// contiguous float4 from LDS.  The next K block is prefetched into registers
+// while the current one is multiplied.
+__global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
+    int ci, cj, klo, khi;
+    if (!band_tile(g, blockIdx.x, blockIdx.y, ci, cj, klo, khi)) return;
+    __shared__ __align__(16) float As[TB * GP];
+    __shared__ __align__(16) float Bs[TB * GP];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wr = w >> 1, wc = w & 1;
+    const int lr = tid >> 4, lc = (tid & 15) * 4;
+    const float *Ab = g.A + (int64_t)ci * TB * g.lda + (int64_t)lr * g.lda + lc;
+    const float *Bb = g.B + (int64_t)cj * TB * g.ldb + (int64_t)lr * g.ldb + lc;
+    const int64_t sa = 16 * g.lda, sb = 16 * g.ldb;
+    float4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define BK_GLOAD(kb)                                                                 \
+    do {                                                                             \
+        const float *a_ = Ab + (kb) * TB;                                            \
+        const float *b_ = Bb + (kb) * TB;                                            \
+        ra0 = *reinterpret_cast<const float4 *>(a_);                                 \
+        ra1 = *reinterpret_cast<const float4 *>(a_ + sa);                            \
+        ra2 = *reinterpret_cast<const float4 *>(a_ + 2 * sa);                        \
+        ra3 = *reinterpret_cast<const float4 *>(a_ + 3 * sa);                        \
+        rb0 = *reinterpret_cast<const float4 *>(b_);                                 \
+        rb1 = *reinterpret_cast<const float4 *>(b_ + sb);                            \
+        rb2 = *reinterpret_cast<const float4 *>(b_ + 2 * sb);                        \
+        rb3 = *reinterpret_cast<const float4 *>(b_ + 3 * sb);                        \
+    } while (0)
+    BK_GLOAD(klo);
+    floatx16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    const float *ap = As + (wr * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
+    const float *bp = Bs + (wc * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
+    float *as_w = As + lr * GP + lc;
+    float *bs_w = Bs + lr * GP + lc;
+    for (int kb = klo; kb <= khi; ++kb) {
+        __syncthreads();
+        *reinterpret_cast<float4 *>(as_w) = ra0;
+        *reinterpret_cast<float4 *>(as_w + 16 * GP) = ra1;
+        *reinterpret_cast<float4 *>(as_w + 32 * GP) = ra2;
+        *reinterpret_cast<float4 *>(as_w + 48 * GP) = ra3;
+        *reinterpret_cast<float4 *>(bs_w) = rb0;
+        *reinterpret_cast<float4 *>(bs_w + 16 * GP) = rb1;
+        *reinterpret_cast<float4 *>(bs_w + 32 * GP) = rb2;
+        *reinterpret_cast<float4 *>(bs_w + 48 * GP) = rb3;
+        __syncthreads();
+        if (kb < khi) BK_GLOAD(kb + 1);
+#pragma unroll
+        for (int s4 = 0; s4 < 8; ++s4) {
+            const float4 av = *reinterpret_cast<const float4 *>(ap + 4 * s4);
+            const float4 bv = *reinterpret_cast<const float4 *>(bp + 4 * s4);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
+        }
+    }
+#undef BK_GLOAD
+    // accumulator layout of the 32 x 32 MFMA: lane l holds column l % 32;
+    // register v holds row 8 (v / 4) + 4 (l / 32) + v % 4.
+    const int col = lane & 31;
+    float *cb = g.C + (int64_t)(ci * TB + wr * 32) * g.ldc + (int64_t)cj * TB + wc * 32 + col;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        float *cp = cb + (int64_t)row * g.ldc;
+        if (g.subtract) *cp -= acc[v];
+        else *cp = acc[v];
+    }
+}
+
+// ----------------------------------------------------------------- finalise
+__global__ __launch_bounds__(256) void sumsq_partial_kernel(const float *__restrict__ x,
+                                                            int64_t count, double *partial) {
+    __shared__ double red[256];
+    const int64_t chunk = (count + NPART - 1) / NPART;
+    const int64_t beg = blockIdx.x * chunk;
+    const int64_t end = min(count, beg + chunk);
+    double s = 0.0;
+    for (int64_t k = beg + threadIdx.x; k < end; k += 256) {
+        const double v = x[k];
+        s += v * v;
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void sumsq_final_kernel(const double *partial, double *out) {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int k = threadIdx.x; k < NPART; k += 256) s += partial[k];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = red[0];
+}
+
+// ---------------------------------------------------------------- schedule
+struct Node {
+    int leaf;  // 1: leaf(K); 0: band(K, L, H)
+    int K, L, H;
+};
+
+void build_nodes(int K, int L, std::vector<Node> &out) {
+    if (L == 1) {
+        out.push_back({1, K, 1, 0});
+        return;
+    }
+    const int H = L / 2;  // split of the range [K, K+L) at K + floor(L/2)
+    build_nodes(K, H, out);
+    out.push_back({0, K, L, H});
+    build_nodes(K + H, L - H, out);
+}
+
+int depth_of(int L) {
+    int d = 0;
+    while (L > 1) {
+        L = L - L / 2;
+        ++d;
+    }
+    return d;
+}
+
+// row range and grid of one band product
+struct Launch {
+    int mode, rlo, rows, cols;
+};
+
+void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Launch &p2) {
+    if (order == BAKRON_ORDER_LA_FIRST) {
+        p1.mode = 0;
+        p1.rlo = std::max(0, K - N + 1);
+        p1.rows = std::min(M - 1, K + H - 1) - p1.rlo + 1;
+        p1.cols = L;
+        p2.mode = 1;
+    } else {
+        p1.mode = 2;
+        p1.rlo = std::max(0, K - M + 1);
+        p1.rows = std::min(N - 1, K + H - 1) - p1.rlo + 1;
+        p1.cols = L;
+        p2.mode = 3;
+    }
+    p2.rlo = std::max(0, K + H - N + 1);
+    p2.rows = std::min(M - 1, K + L - 1) - p2.rlo + 1;
+    p2.cols = L - H;
+}
+
+// executed band flops with dense tiles for one order (host mirror of band_tile)
+double executed_band_flops(int order, int M, int N) {
+    std::vector<Node> nodes;
+    build_nodes(0, M + N - 1, nodes);
+    double macs_tiles = 0;
+    for (const Node &nd : nodes) {
+        if (nd.leaf) continue;
+        Launch p[2];
+        band_launches(order, nd.K, nd.L, nd.H, M, N, p[0], p[1]);
+        for (int s = 0; s < 2; ++s) {
+            for (int y = 0; y < p[s].rows; ++y)
+                for (int x = 0; x < p[s].cols; ++x) {
+                    const int K = nd.K, H = nd.H, row = p[s].rlo + y, o = x;
+                    int lo, hi;
+                    if (p[s].mode == 0) {
+                        const int Jp = K - row + o;
+                        if (Jp < 0 || Jp >= N) continue;
+                        lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1 - row);
+                    } else if (p[s].mode == 2) {
+                        const int Ip = K - row + o;
+                        if (Ip < 0 || Ip >= M) continue;
+                        lo = std::max(0, K - row); hi = std::min(Ip, K + H - 1 - row);
+                    } else {
+                        const int Jp = K + H + o - row;
+                        if (Jp < 0 || Jp >= N) continue;
+                        if (p[s].mode == 1) { lo = std::max(0, K - Jp); hi = std::min(row, K + H - 1); }
+                        else { lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1); }
+                    }
+                    if (hi >= lo) macs_tiles += hi - lo + 1;
+                }
+        }
+    }
+    return macs_tiles * 2.0 * TB * TB * TB;
+}
+
+// Algorithm 6 at single anti-diagonal granularity (product order LA first):
+// per node [k, k+l) split at h, T = E_S LA^T over the band and LB T on R.
+double algorithmic_band_flops(int64_t m, int64_t n) {
+    struct Frame { int64_t k, l; };
+    std::vector<Frame> stack{{0, m + n - 1}};
+    double macs = 0;
+    while (!stack.empty()) {
+        const Frame f = stack.back();
+        stack.pop_back();
+        if (f.l <= 1) continue;
+        const int64_t k = f.k, l = f.l, h = l / 2;
+        stack.push_back({k, h});
+        stack.push_back({k + h, l - h});
+        // T rows i with a source in S; columns jj of the band that some target
+        // row consumes (entries on S diagonals only if a row below reaches R);
+        // count_J = min(jj, b) - a + 1 per entry
+        const int64_t ilo = std::max<int64_t>(0, k - n + 1), ihi = std::min<int64_t>(m - 1, k + h - 1);
+        for (int64_t i = ilo; i <= ihi; ++i) {
+            const int64_t a = std::max<int64_t>(0, k - i);
+            const int64_t b = std::min<int64_t>(n - 1, k + h - 1 - i);
+            const int64_t c = std::min<int64_t>(n - 1, k + l - 1 - i);
+            if (b < a) continue;
+            const int64_t p0 = std::max<int64_t>(a, k + h - m + 1);
+            if (p0 <= b)
+                macs += (double)(b - p0 + 1) * (double)(p0 + b) / 2.0 - (double)(a - 1) * (double)(b - p0 + 1);
+            macs += (double)(c - b) * (double)(b - a + 1);
+        }
+        // targets (i2, jj) in R: count_I = min(i2, k+h-1) - max(0, k-jj) + 1
+        for (int64_t jj = 0; jj < n; ++jj) {
+            const int64_t lo = std::max<int64_t>(0, k + h - jj);
+            const int64_t hi = std::min<int64_t>(m - 1, k + l - 1 - jj);
+            if (hi < lo) continue;
+            const int64_t al = std::max<int64_t>(0, k - jj), be = k + h - 1;
+            const int64_t p = std::min(hi, be);
+            if (lo <= p) macs += (double)(p - lo + 1) * (double)(lo + p) / 2.0 - (double)(al - 1) * (double)(p - lo + 1);
+            const int64_t q = std::max(lo, be + 1);
+            if (q <= hi) macs += (double)(hi - q + 1) * (double)(be - al + 1);
+        }
+    }
+    return 2.0 * macs;
+}
+
+struct ShapeInfo {
+    double exec_flops[3];  // index by order (1, 2)
+    int auto_order;
+};
+
+std::mutex g_shape_mu;
+std::map<std::pair<int, int>, ShapeInfo> g_shapes;
+
+const ShapeInfo &shape_info(int M, int N) {
+    std::lock_guard<std::mutex> lock(g_shape_mu);
+    auto key = std::make_pair(M, N);
+    auto it = g_shapes.find(key);
+    if (it != g_shapes.end()) return it->second;
+    ShapeInfo s{};
+    s.exec_flops[1] = executed_band_flops(BAKRON_ORDER_LA_FIRST, M, N);
+    s.exec_flops[2] = executed_band_flops(BAKRON_ORDER_LB_FIRST, M, N);
+    s.auto_order = s.exec_flops[2] < s.exec_flops[1] ? BAKRON_ORDER_LB_FIRST : BAKRON_ORDER_LA_FIRST;
+    return g_shapes.emplace(key, s).first->second;
+}
+
+thread_local bool g_phase_valid = false;
+thread_local double g_phase_ms[6];
+
+struct Buffers {
+    float *Wp, *Ebuf, *Tbuf, *LAp, *LBp, *sc, *zp;
+    double *partial;
+};
+
+size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
+    Carver cv(ws);
+    float *Wp = cv.take<float>(mp * np);
+    float *Eb = cv.take<float>(mp * np);
+    float *Tb = cv.take<float>(mp * np);
+    float *LAp = cv.take<float>(np * np);
+    float *LBp = cv.take<float>(mp * mp);
+    float *sc = cv.take<float>(mp);
+    float *zp = cv.take<float>(mp);
+    double *part = cv.take<double>(NPART);
+    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, part};
+    return cv.used;
+}
+
+bool valid_quantizer(int32_t kind, int32_t bits) {
+    if (kind == BAKRON_Q_SYM) return bits == 2 || bits == 3 || bits == 4 || bits == 8;
+    if (kind == BAKRON_Q_ASYM) return bits == 2 || bits == 3 || bits == 4;
+    return kind == BAKRON_Q_UNIT;
+}
+
+constexpr int64_t MAX_DIM = int64_t(1) << 20;
+
+}  // namespace
+}  // namespace bakron
+
+using namespace bakron;
+
+extern "C" size_t bakron_quantize_workspace_size(int64_t m, int64_t n, int32_t qkind, int32_t qbits) {
+    if (m < 1 || n < 1 || m > MAX_DIM || n > MAX_DIM || !valid_quantizer(qkind, qbits)) return 0;
+    char *base = reinterpret_cast<char *>(256);  // any aligned address: only sizes matter
+    return carve(base, round_up(m, TB), round_up(n, TB), nullptr);
+}
+
+extern "C" int32_t bakron_schedule_info(int64_t m, int64_t n, int32_t flags, double *out) {
+    clear_error();
+    BK_REQUIRE(out != nullptr, "out is NULL");
+    BK_REQUIRE(m >= 1 && n >= 1 && m <= MAX_DIM && n <= MAX_DIM, "bad shape %lld x %lld",
+               (long long)m, (long long)n);
+    const int M = (int)(round_up(m, TB) / TB), N = (int)(round_up(n, TB) / TB);
+    const ShapeInfo &si = shape_info(M, N);
+    int order = flags & BAKRON_ORDER_MASK;
+    if (order == BAKRON_ORDER_AUTO || order == 3) order = si.auto_order;
+    const int D = M + N - 1;
+    out[0] = TB;
+    out[1] = D;
+    out[2] = 2.0 * (D - 1);
+    out[3] = (double)D * (2 * TB - 1);
+    out[4] = order;
+    out[5] = algorithmic_band_flops(m, n);
+    out[6] = si.exec_flops[order];
+    out[7] = (double)m * (double)n * (double)(m + n);
+    out[8] = (double)M * N * TB * TB * 4.0 * TB;
+    out[9] = depth_of(D);
+    return BAKRON_OK;
+}
+
+extern "C" int32_t bakron_last_phase_ms(double *out) {
+    clear_error();
+    BK_REQUIRE(out != nullptr, "out is NULL");
+    BK_REQUIRE(g_phase_valid, "no timed bakron_quantize call on this thread");
+    for (int k = 0; k < 6; ++k) out[k] = g_phase_ms[k];
+    return BAKRON_OK;
+}
+
+extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
+                                   const float *LB, int32_t qkind, int32_t qbits, int8_t *codes,
+                                   float *scales, float *zeros, float *V, float *E,
+                                   double *sum_e2, int32_t *dev_status, int32_t flags, void *ws,
+                                   size_t ws_bytes, void *stream_) {
+    clear_error();
+    BK_REQUIRE(W && LA && LB && codes && scales, "W, LA, LB, codes and scales must be non-NULL");
+    BK_REQUIRE(m >= 1 && n >= 1 && m <= MAX_DIM && n <= MAX_DIM, "bad shape %lld x %lld",
+               (long long)m, (long long)n);
+    BK_REQUIRE(valid_quantizer(qkind, qbits), "unsupported quantizer kind=%d bits=%d", qkind, qbits);
+    BK_REQUIRE((flags & ~(BAKRON_ORDER_MASK | BAKRON_FLAG_PHASE_TIMING)) == 0 &&
+                   (flags & BAKRON_ORDER_MASK) != 3,
+               "unknown flags 0x%x", flags);
+    const size_t need = bakron_quantize_workspace_size(m, n, qkind, qbits);
+    if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
+        set_error("workspace needs %zu bytes at 256-byte alignment (got %zu at %p)", need,
+                  ws_bytes, ws);
+        return BAKRON_ERR_WORKSPACE;
+    }
+    int32_t st = check_device();
+    if (st != BAKRON_OK) return st;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int64_t mp = round_up(m, TB), np = round_up(n, TB);
+    const int M = (int)(mp / TB), N = (int)(np / TB);
+    const ShapeInfo &si = shape_info(M, N);
+    int order = flags & BAKRON_ORDER_MASK;
+    if (order == BAKRON_ORDER_AUTO) order = si.auto_order;
+    Buffers b;
+    carve(ws, mp, np, &b);
+
+    int qmin, qmax;
+    if (qkind == BAKRON_Q_SYM) { qmin = -(1 << (qbits - 1)); qmax = (1 << (qbits - 1)) - 1; }
+    else if (qkind == BAKRON_Q_ASYM) { qmin = 0; qmax = (1 << qbits) - 1; }
+    else { qmin = -128; qmax = 127; }
+
+    const bool timing = (flags & BAKRON_FLAG_PHASE_TIMING) != 0;
+    std::vector<hipEvent_t> evs;
+    std::vector<int> ev_phase;
+    auto mark = [&](int phase) -> int32_t {
+        if (!timing) return BAKRON_OK;
+        hipEvent_t e;
+        BK_HIP_CHECK(hipEventCreate(&e));
+        BK_HIP_CHECK(hipEventRecord(e, stream));
+        evs.push_back(e);
+        ev_phase.push_back(phase);
+        return BAKRON_OK;
+    };
+    auto release = [&]() {
+        for (hipEvent_t e : evs) (void)hipEventDestroy(e);
+    };
+#define BK_MARK(p)                        \
+    do {                                  \
+        int32_t s_ = mark(p);             \
+        if (s_ != BAKRON_OK) {            \
+            release();                    \
+            return s_;                    \
+        }                                 \
+    } while (0)
+#define BK_LAUNCHED(what)                                                                  \
+    do {                                                                                   \
+        hipError_t e_ = hipGetLastError();                                                 \
+        if (e_ != hipSuccess) {                                                            \
+            set_error("launch of %s failed: %s", what, hipGetErrorString(e_));             \
+            release();                                                                     \
+            return BAKRON_ERR_HIP;                                                         \
+        }                                                                                  \
+    } while (0)
+
+    // phase 0: quantizer parameters + relayout
+    BK_MARK(-1);
+    hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, W, m, n, qkind,
+                       qbits, scales, zeros, b.sc, b.zp, dev_status);
+    BK_LAUNCHED("qparams_kernel");
+    const unsigned rl_blocks = 256u * 8u;
+    const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
+    const int a_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(LA) & 15) == 0);
+    const int b_vec = (m % 4 == 0) && ((reinterpret_cast<uintptr_t>(LB) & 15) == 0);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, W, m, n, b.Wp, mp,
+                       np, 0, w_vec);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LA, n, n, b.LAp,
+                       np, np, 1, a_vec);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LB, m, m, b.LBp,
+                       mp, mp, 1, b_vec);
+    BK_LAUNCHED("relayout_kernel");
+    BK_MARK(0);
+
+    LeafArgs la{b.Wp, b.Ebuf, b.LAp, b.LBp, b.sc, b.zp, mp, np, M, N, order, qmin, qmax,
+                codes, V, E, m, n, dev_status};
+    std::vector<Node> nodes;
+    nodes.reserve(2 * (M + N));
+    build_nodes(0, M + N - 1, nodes);
+    for (const Node &nd : nodes) {
+        if (nd.leaf) {
+            const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
+            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(512), 0, stream, la, nd.K);
+            BK_LAUNCHED("leaf_kernel");
+            BK_MARK(1);
+        } else {
+            Launch p1, p2;
+            band_launches(order, nd.K, nd.L, nd.H, M, N, p1, p2);
+            BandArgs g1{}, g2{};
+            if (order == BAKRON_ORDER_LA_FIRST) {
+                g1 = BandArgs{b.LAp, b.Ebuf, b.Tbuf, np, np, mp, 0, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
+                g2 = BandArgs{b.LBp, b.Tbuf, b.Wp, mp, mp, np, 1, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
+            } else {
+                g1 = BandArgs{b.LBp, b.Ebuf, b.Tbuf, mp, mp, np, 2, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
+                g2 = BandArgs{b.Tbuf, b.LAp, b.Wp, np, np, np, 3, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
+            }
+            if (p1.rows > 0) {
+                hipLaunchKernelGGL(band_gemm_kernel, dim3(p1.cols, p1.rows), dim3(256), 0, stream, g1);
+                BK_LAUNCHED("band_gemm_kernel");
+            }
+            if (p2.rows > 0) {
+                hipLaunchKernelGGL(band_gemm_kernel, dim3(p2.cols, p2.rows), dim3(256), 0, stream, g2);
+                BK_LAUNCHED("band_gemm_kernel");
+            }
+            BK_MARK(2);
+        }
+    }
+    if (sum_e2) {
+        hipLaunchKernelGGL(sumsq_partial_kernel, dim3(NPART), dim3(256), 0, stream, b.Ebuf,
+                           mp * np, b.partial);
+        hipLaunchKernelGGL(sumsq_final_kernel, dim3(1), dim3(256), 0, stream, b.partial, sum_e2);
+        BK_LAUNCHED("sumsq kernels");
+    }
+    BK_MARK(3);
+
+    if (timing) {
+        hipError_t e = hipEventSynchronize(evs.back());
+        if (e != hipSuccess) {
+            set_error("hipEventSynchronize: %s", hipGetErrorString(e));
+            release();
+            return BAKRON_ERR_HIP;
+        }
+        for (int k = 0; k < 6; ++k) g_phase_ms[k] = 0.0;
+        for (size_t k = 1; k < evs.size(); ++k) {
+            float ms = 0.0f;
+            (void)hipEventElapsedTime(&ms, evs[k - 1], evs[k]);
+            const int ph = ev_phase[k];
+            g_phase_ms[ph] += ms;
+            if (ph == 1) g_phase_ms[4] += 1;
+            if (ph == 2) g_phase_ms[5] += 2;
+        }
+        g_phase_valid = true;
+        release();
+    }
+#undef BK_MARK
+#undef BK_LAUNCHED
+    return BAKRON_OK;
+}
