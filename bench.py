@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Benchmark of the two-sided rounding solver (bakron_quantize) on one MI355X.
+
+One step = one bakron_quantize call over the 4096 x 4096 INT4 workload (the
+pages' benchmark size): quantizer parameters, relayout, every leaf and band
+GEMM of the recursion, and the e^2 reduction.  The inputs (W, LA, LB) are
+resident in HBM before timing; LA and LB come from bakron_hessian and
+bakron_factor on the synthetic samples (untimed preparation).
+
+Prints one JSON line.  Besides the contract fields it carries
+  roofline      for the dominant kernel (band GEMM: fp32 MFMA peak), with
+                algorithmic flops / average launch duration from HIP events
+                recorded inside the library on the solver's stream
+  leaf          the leaf phase: HBM bytes per launch, launches, in-kernel steps
+  cpu_baseline  the fp64 oracle (BaKron-naive) on a bounded leading block of
+                the same problem, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_MFMA_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="c3")
+    p.add_argument("--cpu-sample", type=int, default=640,
+                   help="edge of the leading block timed with the CPU oracle (0 = skip)")
+    p.add_argument("--order", type=int, default=0)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    return p.parse_args()
+
+
+def cpu_baseline(W, LA, LB, w, k):
+    """Time BaKron-naive (fp64, OpenMP) on the leading k x k block of the
+    workload: the entries of that block only receive updates from inside it,
+    so it is an exact sub-problem of the same solve."""
+    import oracle
+    Wk = np.ascontiguousarray(W[:k, :k])
+    LAk = np.ascontiguousarray(LA[:k, :k])
+    LBk = np.ascontiguousarray(LB[:k, :k])
+    s, z = oracle.qparams(Wk, w.qkind, w.qbits)
+    oracle._load()
+    t0 = time.perf_counter()
+    oracle.naive(Wk, LAk, LBk, s, z, w.qkind, w.qbits)
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    rate = k * k / dt
+    # the naive solver's work grows as (m(m+1)/2)(n(n+1)/2): its rate on the
+    # whole problem is the sample rate scaled by the work per entry
+    work = lambda a, b: (a * (a + 1) / 2) * (b * (b + 1) / 2)
+    full = (w.m * w.n) / (dt * work(w.m, w.n) / work(k, k))
+    return {"value": rate, "unit": "entries/s", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"leading {k}x{k} block of the {w.m}x{w.n} solve (BaKron-naive fp64, "
+                      f"{dt:.2f} s); full-size rate by the naive work ratio: {full:.4g} entries/s",
+            "seconds": dt, "full_size_rate_estimate": full}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from two_sided_gptq_amd import bakron, synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    bakron.load()
+
+    # ---- synthetic inputs and factors (untimed)
+    W_h = synth.weights(w)
+    X = torch.from_numpy(synth.input_samples(w)).to(dev)
+    Y_h = synth.output_samples(w)
+    LA = bakron.factor(bakron.hessian(X, synth.DAMP))
+    if Y_h is None:
+        LB = torch.eye(w.m, dtype=torch.float32, device=dev)
+    else:
+        LB = bakron.factor(bakron.hessian(torch.from_numpy(Y_h).to(dev), synth.DAMP))
+    del X
+    W = torch.from_numpy(W_h).to(dev)
+    m, n = w.m, w.n
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(bakron.quantize_workspace_size(m, n, w.qkind, w.qbits), dtype=torch.uint8,
+                     device=dev)
+    out = dict(codes=torch.empty((m, n), dtype=torch.int8, device=dev),
+               scales=torch.empty(m, dtype=torch.float32, device=dev),
+               zeros=torch.empty(m, dtype=torch.float32, device=dev) if w.qkind == 1 else None,
+               V=torch.empty((m, n), dtype=torch.float32, device=dev),
+               E=None,
+               sum_e2=torch.empty(1, dtype=torch.float64, device=dev))
+    torch.cuda.synchronize()
+    print(f"[bench] prepared {w.name} {m}x{n}", file=sys.stderr, flush=True)
+
+    def step():
+        bakron.quantize(W, LA, LB, kind=w.qkind, bits=w.qbits, order=args.order,
+                        dev_status=status, workspace=ws, out=out)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    value = m * n * args.steps / elapsed
+    print(f"[bench] timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    if int(status.item()) != 0:
+        raise SystemExit(f"device status {int(status.item())}")
+
+    # ---- per-phase times from HIP events on the solver's stream
+    bakron.quantize(W, LA, LB, kind=w.qkind, bits=w.qbits, order=args.order, dev_status=status,
+                    workspace=ws, out=out, timing=True)
+    ph = bakron.last_phase_ms()
+    sched = bakron.schedule_info(m, n, args.order)
+    band_launches = sched["band_launches"]
+    gemm_avg_s = ph["band_ms"] / 1e3 / band_launches
+    gemm_alg_per_launch = sched["alg_band_flops"] / band_launches
+    gemm_tflops = gemm_alg_per_launch / gemm_avg_s / 1e12
+    leaf_avg_s = ph["leaf_ms"] / 1e3 / sched["leaf_launches"]
+    # leaf algorithmic HBM bytes per entry: W tile in (4), E out (4), codes (1),
+    # V (4), plus the two diagonal 64 x 64 factor blocks per tile (2 x 4 / 64 per entry)
+    leaf_bytes = m * n * (4 + 4 + 1 + 4 + 8.0 / 64)
+    leaf_gbs = leaf_bytes / sched["leaf_launches"] / leaf_avg_s / 1e9
+    dominant = "band_gemm" if ph["band_ms"] >= ph["leaf_ms"] else "leaf"
+    roofline = {"kernel": "band_gemm_kernel", "bound": "mfma", "achieved": gemm_tflops,
+                "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": gemm_tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+                "alg_flops_per_launch": gemm_alg_per_launch, "avg_launch_ms": gemm_avg_s * 1e3,
+                "launches": band_launches}
+
+    result = {
+        "metric": "weight entries quantized/sec at 4096x4096 INT4; % of fp32 MFMA peak",
+        "value": value, "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {m}x{n} W, "
+                               f"{['INT%d sym' % w.qbits, 'INT%d asym' % w.qbits, 'unit'][w.qkind]}, "
+                               f"A from {w.n_x} samples, B from {w.n_y} samples",
+                   "m": m, "n": n, "qkind": w.qkind, "qbits": w.qbits,
+                   "order": int(sched["order"]), "tile": int(sched["tile"])},
+        "roofline": roofline,
+        "dominant_kernel": dominant,
+        "gemm_pct_fp32_mfma_peak": 100.0 * gemm_tflops / FP32_MFMA_PEAK_TFLOPS,
+        "whole_solve_tflops_alg": sched["alg_band_flops"] / (ms / 1e3) / 1e12,
+        "phases_ms": {k: ph[k] for k in ("prep_ms", "leaf_ms", "band_ms", "final_ms")},
+        "leaf": {"launches": int(sched["leaf_launches"]), "in_kernel_steps": int(sched["leaf_steps"]),
+                 "avg_launch_ms": leaf_avg_s * 1e3, "alg_bytes": leaf_bytes,
+                 "achieved_GBs": leaf_gbs, "hbm_frac": leaf_gbs / HBM_PEAK_GBS},
+        "schedule": sched,
+    }
+    if args.cpu_sample > 0:
+        LA_h = LA.cpu().numpy()
+        LB_h = LB.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(W_h, LA_h, LB_h, w, min(args.cpu_sample, m, n))
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

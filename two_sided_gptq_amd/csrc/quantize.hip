@@ -31,7 +31,7 @@ namespace bakron {
 namespace {
 
 constexpr int TB = 64;  // tile edge (leaf tile and band-GEMM output tile)
-constexpr int LP = 68;  // LDS row stride in floats for the leaf tiles
+constexpr int LP = 80;  // LDS row stride in floats for the leaf tiles
 constexpr int GP = 68;  // LDS row stride in floats for the GEMM operand tiles
 constexpr int NPART = 1024;  // partial sums of the e^2 reduction
 
@@ -152,23 +152,18 @@ struct LeafArgs {
     int32_t *dev_status;
 };
 
-// sum over the 8 consecutive lanes of a group (all 8 end with the total)
-__device__ inline float group8_sum(float x) {
+// sum over the 4 consecutive lanes of a group (all 4 end with the total)
+__device__ inline float group4_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
     return x;
 }
 
-__device__ inline float dot8(const float4 a0, const float4 a1, const float4 b0, const float4 b1) {
-    float s = a0.x * b0.x;
-    s = fmaf(a0.y, b0.y, s);
-    s = fmaf(a0.z, b0.z, s);
-    s = fmaf(a0.w, b0.w, s);
-    s = fmaf(a1.x, b1.x, s);
-    s = fmaf(a1.y, b1.y, s);
-    s = fmaf(a1.z, b1.z, s);
-    s = fmaf(a1.w, b1.w, s);
+__device__ inline float dot4(const float4 a, const float4 b, float s) {
+    s = fmaf(a.x, b.x, s);
+    s = fmaf(a.y, b.y, s);
+    s = fmaf(a.z, b.z, s);
+    s = fmaf(a.w, b.w, s);
     return s;
 }
 
@@ -176,92 +171,304 @@ __device__ inline float dot8(const float4 a0, const float4 a1, const float4 b0, 
 // the diagonal blocks LB[I,I], LA[J,J].  It is solved in the order-free form
 // (each entry's value before rounding is W minus the contributions of every
 // entry before it in the product order):
-//   Z[r][c] = sum_{c' <= c} E[r][c'] LA[c][c']          (row direction)
-//   P[r][c] = W[r][c] - LB[r][r] sum_{c' < c} E[r][c'] LA[c][c']
-//                     - sum_{r' < r} LB[r][r'] Z[r'][c]  (column direction)
-// Step d rounds the in-tile anti-diagonal r + c = d; each of its entries is
-// handled by 8 lanes (two length-64 dot products split 8 ways, then a DPP
-// reduction).  E and Z start at zero, so the dots run over full rows and the
-// not-yet-computed terms contribute exact zeros.
-__global__ __launch_bounds__(512) void leaf_kernel(LeafArgs a, int K) {
-    __shared__ __align__(16) float Ws[TB * LP];
-    __shared__ __align__(16) float Es[TB * LP];
-    __shared__ __align__(16) float Zs[TB * LP];  // Zs[c][r] = Z[r][c]
-    __shared__ __align__(16) float Bs[TB * LP];  // LB[I,I]
-    __shared__ __align__(16) float As[TB * LP];  // LA[J,J]
-    __shared__ float s_sc[TB], s_isc[TB], s_zp[TB], s_ib[TB], s_ia[TB];
-    __shared__ int8_t Cs[TB * TB];
+//   Z[r][c] = sum_{k <= c} E[r][k] LA[c][k]                  (row direction)
+//   P[r][c] = W[r][c] - LB[r][r] sum_{k < c} E[r][k] LA[c][k]
+//                     - sum_{k < r} LB[r][k] Z[k][c]         (column direction)
+// Step d rounds the in-tile anti-diagonal r + c = d.  Each entry is handled by
+// a group of 4 lanes: lane q takes the float4 chunks 4j + q (j = 0..3) of the
+// two length-64 dot products; a 2-step DPP butterfly gives all 4 lanes the
+// sums and every lane of the group rounds (no broadcast needed).
+//
+// Only two terms of an entry's dots come from the step just before it:
+// E[r][c-1] LA[c][c-1] and LB[r][r-1] Z[r-1][c].  Everything else is at least
+// two steps old, so the operands of both dots for step d+1 are loaded during
+// step d (double-buffered registers) and summed at the start of step d+1
+// while the one fresh neighbour value is in flight:
+//   steps 0..63:   group g owns row g (its LB row is kept in registers with
+//                  element g-1 zeroed; the fresh Z[g-1][c] is read after the
+//                  barrier; its own E[g][c-1] is still in a register);
+//   steps 64..126: group g owns column 63-g (its LA row in registers with
+//                  element c-1 zeroed; fresh E[r][c-1] read after the
+//                  barrier; its own Z[r-1][c] still in a register).
+// A load of the group's own row/column never sees the value the group writes
+// later in the same step (LDS operations of one wave complete in order), and
+// the value a neighbouring group may be writing meanwhile is multiplied by
+// the zeroed register element.  E and Z start at zero and the factors are
+// lower triangular, so 16-wide chunks beyond a wave's largest column (first
+// dot) or row (second dot) are exact zeros and are not loaded.  Those chunk
+// counts depend only on the wave and on a 16-step segment of d, so each
+// (wave, segment) pair is its own template instance: every LDS wait count is
+// static and the critical read never waits for the operand loads behind it.
+// Rows of the LDS tiles are 80 floats apart, so four consecutive rows occupy
+// disjoint 64-byte bank groups.
+constexpr int LQ = LP / 4;  // LDS row stride in float4
 
+__shared__ __align__(16) float lf_W[TB * LP];
+__shared__ __align__(16) float lf_E[TB * LP];
+__shared__ __align__(16) float lf_Z[TB * LP];  // lf_Z[c][k] = Z[k][c]
+__shared__ __align__(16) float lf_B[TB * LP];  // LB[I,I]
+__shared__ __align__(16) float lf_A[TB * LP];  // LA[J,J]
+__shared__ float4 lf_row[TB];                  // (s, 1/s, z, 1/LB_rr)
+__shared__ float2 lf_col[TB];                  // (LA_cc, 1/LA_cc)
+__shared__ int8_t lf_C[TB * TB];
+
+struct Bulk {
+    float4 x[4], y[4], z[4];
+};
+
+struct Lane {
+    int g, q;
+    float qminf, qmaxf;
+    int bad;
+};
+
+__device__ __forceinline__ float4 f4(int i, const float *base) {
+    return reinterpret_cast<const float4 *>(base)[i];
+}
+
+// zero component t of a float4 (t in 0..3; any other value leaves it)
+__device__ inline float4 zero_component(float4 v, int t) {
+    v.x = t == 0 ? 0.0f : v.x;
+    v.y = t == 1 ? 0.0f : v.y;
+    v.z = t == 2 ? 0.0f : v.z;
+    v.w = t == 3 ? 0.0f : v.w;
+    return v;
+}
+
+// round entry (r, c) given its dot products; writes E, Z and the code; returns e
+__device__ __forceinline__ float leaf_round(Lane &L, int r, int c, float wv, float lbd, float d1,
+                                            float d2, float4 rc, float2 cc, float &zv) {
+    const float P = wv - lbd * d1 - d2;
+    const float cz = fminf(fmaxf(rintf(P * rc.y) + rc.z, L.qminf), L.qmaxf);
+    const float v = rc.x * (cz - rc.z);
+    const float e = (P - v) * (rc.w * cc.y);
+    zv = fmaf(e, cc.x, d1);
+    L.bad |= !isfinite(e);
+    if (L.q == 0) {
+        lf_E[r * LP + c] = e;
+        lf_Z[c * LP + r] = zv;
+        lf_C[r * TB + c] = (int8_t)(int)cz;
+    }
+    return e;
+}
+
+// steps 0..63: group g owns row r = g.  Loads the operands for step d + 1 into
+// nxt; with COMPUTE, rounds this step's entry from cur.
+template <int NJ1, int NJ2, bool COMPUTE>
+__device__ __forceinline__ void p1_step(Lane &L, int d, const float4 (&lbm)[4], float lb_last,
+                                        float lbd, float4 rc, float &e_prev, Bulk &cur,
+                                        Bulk &nxt) {
+    const int r = L.g, q = L.q;
+    const bool act = COMPUTE && r <= d;
+    const int c = act ? d - r : 0;
+    float zc = 0.0f, wv = 0.0f, la_last = 0.0f;
+    float2 cc = make_float2(1.0f, 1.0f);
+    if (COMPUTE) {
+        zc = lf_Z[c * LP + max(r - 1, 0)];
+        wv = lf_W[r * LP + c];
+        cc = lf_col[c];
+        la_last = lf_A[c * LP + max(c - 1, 0)];
+    }
+    // keep the fresh read ahead of the operand loads in the in-order LDS queue
+    __builtin_amdgcn_sched_barrier(0);
+    const int cn = min(max(d + 1 - r, 0), TB - 1);
+#pragma unroll
+    for (int j = 0; j < NJ1; ++j) {
+        nxt.x[j] = f4(r * LQ + 4 * j + q, lf_E);
+        nxt.y[j] = f4(cn * LQ + 4 * j + q, lf_A);
+    }
+    if (NJ1 < 4) nxt.x[NJ1 < 4 ? NJ1 : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < NJ2; ++j) nxt.z[j] = f4(cn * LQ + 4 * j + q, lf_Z);
+    if (COMPUTE) {
+        float n1 = 0.0f, n2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ1; ++j) n1 = dot4(cur.x[j], cur.y[j], n1);
+#pragma unroll
+        for (int j = 0; j < NJ2; ++j) n2 = dot4(lbm[j], cur.z[j], n2);
+        const float b1 = group4_sum(n1), b2 = group4_sum(n2);
+        if (act) {
+            float zv;
+            e_prev = leaf_round(L, r, c, wv, lbd, fmaf(e_prev, la_last, b1), fmaf(lb_last, zc, b2),
+                                rc, cc, zv);
+        }
+    }
+    __syncthreads();
+}
+
+template <int W, int S>
+__device__ __forceinline__ void p1_segment(Lane &L, const float4 (&lbm)[4], float lb_last,
+                                           float lbd, float4 rc, float &e_prev, Bulk &A, Bulk &B) {
+    constexpr int d0 = 16 * S;
+    if constexpr (S + 1 < W) {
+        for (int i = 0; i < 16; ++i) __syncthreads();
+    } else if constexpr (S + 1 == W) {
+        for (int i = 0; i < 15; ++i) __syncthreads();
+        p1_step<0, W + 1, false>(L, d0 + 15, lbm, lb_last, lbd, rc, e_prev, B, A);
+    } else {
+        constexpr int NJ1 = S - W + 1, NJ2 = W + 1;
+        for (int i = 0; i < 16; i += 2) {
+            p1_step<NJ1, NJ2, true>(L, d0 + i, lbm, lb_last, lbd, rc, e_prev, A, B);
+            p1_step<NJ1, NJ2, true>(L, d0 + i + 1, lbm, lb_last, lbd, rc, e_prev, B, A);
+        }
+    }
+    if constexpr (S < 3) p1_segment<W, S + 1>(L, lbm, lb_last, lbd, rc, e_prev, A, B);
+}
+
+// steps 64..126: group g owns column c = 63 - g, row r = d - c
+template <int NJ1, int NJ2>
+__device__ __forceinline__ void p2_step(Lane &L, int d, bool wave_act, const float4 (&lam)[4],
+                                        float la_last, float2 cc, float &z_prev, Bulk &cur,
+                                        Bulk &nxt) {
+    const int c = TB - 1 - L.g, q = L.q;
+    if (wave_act) {
+        const bool act = L.g <= 2 * TB - 2 - d;
+        const int r = act ? d - c : TB - 1;
+        const float ec = lf_E[r * LP + max(c - 1, 0)];
+        const float wv = lf_W[r * LP + c];
+        const float4 rc = lf_row[r];
+        const float lbd = lf_B[r * LP + r];
+        const float lb_last = lf_B[r * LP + r - 1];
+        // keep the fresh read ahead of the operand loads in the in-order LDS queue
+        __builtin_amdgcn_sched_barrier(0);
+        const int rn = min(r + 1, TB - 1);
+#pragma unroll
+        for (int j = 0; j < NJ1; ++j) nxt.x[j] = f4(rn * LQ + 4 * j + q, lf_E);
+#pragma unroll
+        for (int j = 0; j < NJ2; ++j) {
+            nxt.y[j] = f4(rn * LQ + 4 * j + q, lf_B);
+            nxt.z[j] = f4(c * LQ + 4 * j + q, lf_Z);
+        }
+        if (NJ2 < 4) nxt.y[NJ2 < 4 ? NJ2 : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        float n1 = 0.0f, n2 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ1; ++j) n1 = dot4(cur.x[j], lam[j], n1);
+#pragma unroll
+        for (int j = 0; j < NJ2; ++j) n2 = dot4(cur.y[j], cur.z[j], n2);
+        const float b1 = group4_sum(n1), b2 = group4_sum(n2);
+        if (act) {
+            float zv;
+            leaf_round(L, r, c, wv, lbd, fmaf(ec, la_last, b1), fmaf(lb_last, z_prev, b2), rc, cc,
+                       zv);
+            z_prev = zv;
+        }
+    }
+    __syncthreads();
+}
+
+template <int W, int K>
+__device__ __forceinline__ void p2_segment(Lane &L, const float4 (&lam)[4], float la_last,
+                                           float2 cc, float &z_prev, Bulk &A, Bulk &B) {
+    constexpr int t0 = 16 * K;
+    constexpr int len = K < 3 ? 16 : 15;
+    constexpr int NJ1 = 4 - W;
+    constexpr int NJ2 = (W + 2 + K < 4) ? (W + 2 + K) : 4;
+    constexpr int last = 62 - 16 * W;  // last active t of this wave
+    for (int i = 0; i + 1 < len; i += 2) {
+        p2_step<NJ1, NJ2>(L, TB + t0 + i, t0 + i <= last, lam, la_last, cc, z_prev, A, B);
+        p2_step<NJ1, NJ2>(L, TB + t0 + i + 1, t0 + i + 1 <= last, lam, la_last, cc, z_prev, B, A);
+    }
+    if constexpr (len & 1)
+        p2_step<NJ1, NJ2>(L, TB + t0 + len - 1, t0 + len - 1 <= last, lam, la_last, cc, z_prev, A, B);
+    if constexpr (K < 3) p2_segment<W, K + 1>(L, lam, la_last, cc, z_prev, A, B);
+}
+
+template <int W>
+__device__ __forceinline__ void leaf_sweep(Lane &L) {
+    const int g = L.g, q = L.q;
+    Bulk A, B;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        A.x[j] = A.y[j] = A.z[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        B.x[j] = B.y[j] = B.z[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    {   // steps 0..63
+        const int r = g;
+        float4 lbm[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lbm[j] = zero_component(f4(r * LQ + 4 * j + q, lf_B),
+                                    (r >= 1 && (((r - 1) >> 4) == j) && ((((r - 1) >> 2) & 3) == q))
+                                        ? ((r - 1) & 3) : 4);
+        const float lb_last = r >= 1 ? lf_B[r * LP + r - 1] : 0.0f;
+        const float lbd = lf_B[r * LP + r];
+        const float4 rc = lf_row[r];
+        float e_prev = 0.0f;
+        p1_segment<W, 0>(L, lbm, lb_last, lbd, rc, e_prev, A, B);
+    }
+    {   // steps 64..126
+        const int c = TB - 1 - g;
+        float4 lam[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lam[j] = zero_component(f4(c * LQ + 4 * j + q, lf_A),
+                                    (c >= 1 && (((c - 1) >> 4) == j) && ((((c - 1) >> 2) & 3) == q))
+                                        ? ((c - 1) & 3) : 4);
+        const float la_last = c >= 1 ? lf_A[c * LP + c - 1] : 0.0f;
+        const float2 cc = lf_col[c];
+        // operands for step 64: entry (g + 1, c), every E and Z so far is visible
+        const int rp = min(g + 1, TB - 1);
+        constexpr int NJ1 = 4 - W, NJ2 = W + 1;
+#pragma unroll
+        for (int j = 0; j < NJ1; ++j) A.x[j] = f4(rp * LQ + 4 * j + q, lf_E);
+#pragma unroll
+        for (int j = 0; j < NJ2; ++j) {
+            A.y[j] = f4(rp * LQ + 4 * j + q, lf_B);
+            A.z[j] = f4(c * LQ + 4 * j + q, lf_Z);
+        }
+        if (NJ2 < 4) A.y[NJ2 < 4 ? NJ2 : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        float z_prev = 0.0f;  // the prologue's operands already include Z[g][c]
+        p2_segment<W, 0>(L, lam, la_last, cc, z_prev, A, B);
+    }
+}
+
+__global__ __launch_bounds__(256) void leaf_kernel(LeafArgs a, int K) {
     const int tid = threadIdx.x;
     const int Ilo = max(0, K - a.N + 1);
     const int I = Ilo + blockIdx.x;
     const int J = K - I;
     const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
 
-    for (int idx = tid; idx < TB * 16; idx += 512) {
+    for (int idx = tid; idx < TB * 16; idx += 256) {
         const int r = idx >> 4, c4 = (idx & 15) * 4;
-        *reinterpret_cast<float4 *>(Ws + r * LP + c4) =
+        *reinterpret_cast<float4 *>(lf_W + r * LP + c4) =
             *reinterpret_cast<const float4 *>(a.Wp + (r0 + r) * a.np + c0 + c4);
-        *reinterpret_cast<float4 *>(Bs + r * LP + c4) =
+        *reinterpret_cast<float4 *>(lf_B + r * LP + c4) =
             *reinterpret_cast<const float4 *>(a.LBp + (r0 + r) * a.mp + r0 + c4);
-        *reinterpret_cast<float4 *>(As + r * LP + c4) =
+        *reinterpret_cast<float4 *>(lf_A + r * LP + c4) =
             *reinterpret_cast<const float4 *>(a.LAp + (c0 + r) * a.np + c0 + c4);
-        *reinterpret_cast<float4 *>(Es + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4 *>(Zs + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (tid < TB) {
-        const float s = a.sc[r0 + tid];
-        s_sc[tid] = s;
-        s_isc[tid] = 1.0f / s;
-        s_zp[tid] = a.zp[r0 + tid];
+        *reinterpret_cast<float4 *>(lf_E + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4 *>(lf_Z + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
     if (tid < TB) {
-        s_ib[tid] = 1.0f / Bs[tid * LP + tid];
-        s_ia[tid] = 1.0f / As[tid * LP + tid];
+        const float s = a.sc[r0 + tid];
+        lf_row[tid] = make_float4(s, 1.0f / s, a.zp[r0 + tid], 1.0f / lf_B[tid * LP + tid]);
+        const float la = lf_A[tid * LP + tid];
+        lf_col[tid] = make_float2(la, 1.0f / la);
     }
     __syncthreads();
 
-    const int g = tid >> 3, q = tid & 7;
-    const float qminf = (float)a.qmin, qmaxf = (float)a.qmax;
-    int bad = 0;
-    for (int d = 0; d < 2 * TB - 1; ++d) {
-        const int rlo = d < TB ? 0 : d - TB + 1;
-        const int rhi = d < TB ? d : TB - 1;
-        const int r = min(rlo + g, rhi);
-        const bool act = (rlo + g) <= rhi;
-        const int c = d - r;
-        const float4 *e4 = reinterpret_cast<const float4 *>(Es + r * LP);
-        const float4 *a4 = reinterpret_cast<const float4 *>(As + c * LP);
-        const float4 *b4 = reinterpret_cast<const float4 *>(Bs + r * LP);
-        const float4 *z4 = reinterpret_cast<const float4 *>(Zs + c * LP);
-        float d1 = dot8(e4[q], e4[8 + q], a4[q], a4[8 + q]);
-        float d2 = dot8(b4[q], b4[8 + q], z4[q], z4[8 + q]);
-        d1 = group8_sum(d1);
-        d2 = group8_sum(d2);
-        if (act && q == 0) {
-            const float P = Ws[r * LP + c] - Bs[r * LP + r] * d1 - d2;
-            const float u = P * s_isc[r];
-            const float cz = fminf(fmaxf(rintf(u) + s_zp[r], qminf), qmaxf);
-            const float v = s_sc[r] * (cz - s_zp[r]);
-            const float e = (P - v) * (s_ib[r] * s_ia[c]);
-            bad |= !isfinite(e);
-            Es[r * LP + c] = e;
-            Zs[c * LP + r] = fmaf(e, As[c * LP + c], d1);
-            Cs[r * TB + c] = (int8_t)(int)cz;
-        }
-        __syncthreads();
-    }
+    Lane L{tid >> 2, tid & 3, (float)a.qmin, (float)a.qmax, 0};
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (w == 0) leaf_sweep<0>(L);
+    else if (w == 1) leaf_sweep<1>(L);
+    else if (w == 2) leaf_sweep<2>(L);
+    else leaf_sweep<3>(L);
+    const float *Es = lf_E;
+    const int8_t *Cs = lf_C;
+    const float4 *s_row = lf_row;
+    const int bad = L.bad;
 
     // E tile to the band-update buffer
     if (a.order == BAKRON_ORDER_LA_FIRST) {
-        for (int idx = tid; idx < TB * 16; idx += 512) {
+        for (int idx = tid; idx < TB * 16; idx += 256) {
             const int r = idx >> 4, c4 = (idx & 15) * 4;
             *reinterpret_cast<float4 *>(a.Ebuf + (r0 + r) * a.np + c0 + c4) =
                 *reinterpret_cast<const float4 *>(Es + r * LP + c4);
         }
     } else {
-        for (int idx = tid; idx < TB * 16; idx += 512) {
+        for (int idx = tid; idx < TB * 16; idx += 256) {
             const int c = idx >> 4, rr4 = (idx & 15) * 4;
             *reinterpret_cast<float4 *>(a.Ebuf + (c0 + c) * a.mp + r0 + rr4) =
                 make_float4(Es[(rr4 + 0) * LP + c], Es[(rr4 + 1) * LP + c],
@@ -269,13 +476,14 @@ __global__ __launch_bounds__(512) void leaf_kernel(LeafArgs a, int K) {
         }
     }
     // caller-visible outputs
-    for (int idx = tid; idx < TB * TB; idx += 512) {
+    for (int idx = tid; idx < TB * TB; idx += 256) {
         const int r = idx >> 6, c = idx & 63;
         const int64_t gi = r0 + r, gj = c0 + c;
         if (gi < a.m && gj < a.n) {
             const int8_t code = Cs[r * TB + c];
             a.codes[gi * a.n + gj] = code;
-            if (a.V) a.V[gi * a.n + gj] = s_sc[r] * ((float)code - s_zp[r]);
+            const float4 rc = s_row[r];
+            if (a.V) a.V[gi * a.n + gj] = rc.x * ((float)code - rc.z);
             if (a.E) a.E[gi * a.n + gj] = Es[r * LP + c];
         }
     }
@@ -746,7 +954,7 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     for (const Node &nd : nodes) {
         if (nd.leaf) {
             const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
-            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(512), 0, stream, la, nd.K);
+            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(256), 0, stream, la, nd.K);
             BK_LAUNCHED("leaf_kernel");
             BK_MARK(1);
         } else {
