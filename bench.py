@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=640,
                    help="edge of the leading block timed with the CPU oracle (0 = skip)")
     p.add_argument("--order", type=int, default=0)
+    p.add_argument("--eager", action="store_true",
+                   help="launch kernel by kernel instead of replaying the solve's graph")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -110,7 +112,7 @@ def main():
 
     def step():
         bakron.quantize(W, LA, LB, kind=w.qkind, bits=w.qbits, order=args.order,
-                        dev_status=status, workspace=ws, out=out)
+                        dev_status=status, workspace=ws, out=out, graph=not args.eager)
 
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -162,7 +164,8 @@ def main():
                                f"{['INT%d sym' % w.qbits, 'INT%d asym' % w.qbits, 'unit'][w.qkind]}, "
                                f"A from {w.n_x} samples, B from {w.n_y} samples",
                    "m": m, "n": n, "qkind": w.qkind, "qbits": w.qbits,
-                   "order": int(sched["order"]), "tile": int(sched["tile"])},
+                   "order": int(sched["order"]), "tile": int(sched["tile"]),
+                   "launch": "eager" if args.eager else "graph"},
         "roofline": roofline,
         "dominant_kernel": dominant,
         "gemm_pct_fp32_mfma_peak": 100.0 * gemm_tflops / FP32_MFMA_PEAK_TFLOPS,

@@ -75,6 +75,8 @@ extern "C" {
 #define BAKRON_FLAG_PHASE_TIMING 4 /* time each phase with HIP events; the call
                                       then synchronises the stream before it
                                       returns.  See bakron_last_phase_ms(). */
+#define BAKRON_FLAG_NO_GRAPH 8     /* launch kernel by kernel instead of replaying
+                                      the cached executable graph of the solve */
 
 /*
  * bakron_hessian -- Kronecker factor from samples, with damping.
@@ -120,6 +122,11 @@ int32_t bakron_factor(const float *H, int64_t d, float *L, int32_t *dev_status,
  * Any m, n >= 1 is accepted; inside, W is handled in 64 x 64 tiles with
  * zero padding.  The result equals the raster-order naive solver up to fp32
  * rounding order (Theorem 3.2).
+ * The static schedule of a solve is captured once into an executable HIP graph,
+ * cached per (device, sizes, quantizer, order, every pointer argument, ws) --
+ * at most 16 graphs, least recently used dropped -- and replayed on `stream`.
+ * The first call with a new key pays the capture.  Not thread-safe across
+ * concurrent calls that share a workspace (they race on it anyway).
  */
 size_t bakron_quantize_workspace_size(int64_t m, int64_t n, int32_t qkind, int32_t qbits);
 int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,

@@ -138,3 +138,36 @@ def test_nonfinite_flag(bk):
     A, B, LA, LB = _factors(X, Y, 64)
     res = _gpu(bk, W, LA, LB, synth.SYM, 4)
     assert res["status"] & bk.DEV_NONFINITE
+
+
+def test_graph_replay_matches_eager(bk):
+    """The cached graph of a solve reads the buffers' current contents: replays
+    with new data in the same buffers match eager launches bit for bit, with
+    eager work and synchronisations between the replays."""
+    m, n = 192, 256
+    W1, X, Y = synth.custom(m, n, 901)
+    W2, _, _ = synth.custom(m, n, 902)
+    A, B, LA, LB = _factors(X, Y, m)
+    dev = torch.device("cuda:0")
+    Wd = torch.from_numpy(W1).to(dev)
+    LAd, LBd = torch.from_numpy(LA).to(dev), torch.from_numpy(LB).to(dev)
+    ws = torch.empty(bk.quantize_workspace_size(m, n, 0, 4), dtype=torch.uint8, device=dev)
+    out = dict(codes=torch.empty((m, n), dtype=torch.int8, device=dev),
+               scales=torch.empty(m, device=dev), zeros=None,
+               V=torch.empty((m, n), device=dev), E=torch.empty((m, n), device=dev),
+               sum_e2=torch.empty(1, dtype=torch.float64, device=dev))
+
+    def run(W_host, graph):
+        Wd.copy_(torch.from_numpy(W_host))
+        bk.quantize(Wd, LAd, LBd, workspace=ws, out=out, graph=graph)
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy().copy() for k, v in out.items() if v is not None}
+
+    ref1, ref2 = run(W1, False), run(W2, False)
+    for rep in range(3):
+        for W_host, ref in ((W1, ref1), (W2, ref2)):
+            got = run(W_host, True)
+            for k in ref:
+                assert np.array_equal(got[k], ref[k]), (rep, k)
+            # eager work between replays
+            run(W_host, False)

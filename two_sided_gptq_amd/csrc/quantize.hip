@@ -596,13 +596,18 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
     // accumulator layout of the 32 x 32 MFMA: lane l holds column l % 32;
     // register v holds row 8 (v / 4) + 4 (l / 32) + v % 4.
     const int col = lane & 31;
-    float *cb = g.C + (int64_t)(ci * TB + wr * 32) * g.ldc + (int64_t)cj * TB + wc * 32 + col;
+    float *cb = g.C + (int64_t)(ci * TB + wr * 32 + 4 * (lane >> 5)) * g.ldc + (int64_t)cj * TB +
+                wc * 32 + col;
+    if (g.subtract) {
+        // all 16 old values in flight at once, then the stores
+        float old[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        float *cp = cb + (int64_t)row * g.ldc;
-        if (g.subtract) *cp -= acc[v];
-        else *cp = acc[v];
+        for (int v = 0; v < 16; ++v) old[v] = cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc] = old[v] - acc[v];
+    } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc] = acc[v];
     }
 }
 
@@ -859,6 +864,189 @@ extern "C" int32_t bakron_last_phase_ms(double *out) {
     return BAKRON_OK;
 }
 
+namespace bakron {
+namespace {
+
+// Everything one solve enqueues, given validated arguments.
+struct Solve {
+    const float *W, *LA, *LB;
+    int64_t m, n, mp, np;
+    int M, N, order, qkind, qbits, qmin, qmax;
+    int8_t *codes;
+    float *scales, *zeros, *V, *E;
+    double *sum_e2;
+    int32_t *dev_status;
+    Buffers b;
+};
+
+// Enqueues the whole solve on `stream`.  With `marks`, records an event after
+// each phase (-1 start, 0 prep, 1 leaf, 2 band node, 3 finalise).
+int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_t> *evs,
+                      std::vector<int> *ev_phase) {
+    auto mark = [&](int phase) -> int32_t {
+        if (!evs) return BAKRON_OK;
+        hipEvent_t e;
+        BK_HIP_CHECK(hipEventCreate(&e));
+        evs->push_back(e);
+        ev_phase->push_back(phase);
+        BK_HIP_CHECK(hipEventRecord(e, stream));
+        return BAKRON_OK;
+    };
+#define BK_MARK(p)                    \
+    do {                              \
+        int32_t s_ = mark(p);         \
+        if (s_ != BAKRON_OK) return s_; \
+    } while (0)
+    const Buffers &b = sv.b;
+    const int M = sv.M, N = sv.N;
+    const int64_t m = sv.m, n = sv.n, mp = sv.mp, np = sv.np;
+    BK_MARK(-1);
+    hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, sv.W, m, n,
+                       sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status);
+    BK_LAUNCH_CHECK("qparams_kernel");
+    const unsigned rl_blocks = 256u * 8u;
+    const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.W) & 15) == 0);
+    const int a_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LA) & 15) == 0);
+    const int b_vec = (m % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LB) & 15) == 0);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.W, m, n, b.Wp,
+                       mp, np, 0, w_vec);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LA, n, n, b.LAp,
+                       np, np, 1, a_vec);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LB, m, m, b.LBp,
+                       mp, mp, 1, b_vec);
+    BK_LAUNCH_CHECK("relayout_kernel");
+    BK_MARK(0);
+
+    LeafArgs la{b.Wp, b.Ebuf, b.LAp, b.LBp, b.sc, b.zp, mp, np, M, N, sv.order, sv.qmin, sv.qmax,
+                sv.codes, sv.V, sv.E, m, n, sv.dev_status};
+    std::vector<Node> nodes;
+    nodes.reserve(2 * (M + N));
+    build_nodes(0, M + N - 1, nodes);
+    for (const Node &nd : nodes) {
+        if (nd.leaf) {
+            const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
+            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(256), 0, stream, la, nd.K);
+            BK_LAUNCH_CHECK("leaf_kernel");
+            BK_MARK(1);
+        } else {
+            Launch p1, p2;
+            band_launches(sv.order, nd.K, nd.L, nd.H, M, N, p1, p2);
+            BandArgs g1{}, g2{};
+            if (sv.order == BAKRON_ORDER_LA_FIRST) {
+                g1 = BandArgs{b.LAp, b.Ebuf, b.Tbuf, np, np, mp, 0, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
+                g2 = BandArgs{b.LBp, b.Tbuf, b.Wp, mp, mp, np, 1, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
+            } else {
+                g1 = BandArgs{b.LBp, b.Ebuf, b.Tbuf, mp, mp, np, 2, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
+                g2 = BandArgs{b.Tbuf, b.LAp, b.Wp, np, np, np, 3, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
+            }
+            if (p1.rows > 0) {
+                hipLaunchKernelGGL(band_gemm_kernel, dim3(p1.cols, p1.rows), dim3(256), 0, stream, g1);
+                BK_LAUNCH_CHECK("band_gemm_kernel");
+            }
+            if (p2.rows > 0) {
+                hipLaunchKernelGGL(band_gemm_kernel, dim3(p2.cols, p2.rows), dim3(256), 0, stream, g2);
+                BK_LAUNCH_CHECK("band_gemm_kernel");
+            }
+            BK_MARK(2);
+        }
+    }
+    if (sv.sum_e2) {
+        hipLaunchKernelGGL(sumsq_partial_kernel, dim3(NPART), dim3(256), 0, stream, b.Ebuf,
+                           mp * np, b.partial);
+        hipLaunchKernelGGL(sumsq_final_kernel, dim3(1), dim3(256), 0, stream, b.partial, sv.sum_e2);
+        BK_LAUNCH_CHECK("sumsq kernels");
+    }
+    BK_MARK(3);
+#undef BK_MARK
+    return BAKRON_OK;
+}
+
+// Executable graphs of whole solves, keyed by every argument the kernels bake
+// in (device, pointers, sizes, quantizer, product order).  A replay reads the
+// buffers' current contents.  At most kGraphCache entries; the least recently
+// used one is dropped.
+struct GraphKey {
+    int dev, order, qkind, qbits;
+    int64_t m, n;
+    const void *p[12];
+    bool operator<(const GraphKey &o) const {
+        if (dev != o.dev) return dev < o.dev;
+        if (order != o.order) return order < o.order;
+        if (qkind != o.qkind) return qkind < o.qkind;
+        if (qbits != o.qbits) return qbits < o.qbits;
+        if (m != o.m) return m < o.m;
+        if (n != o.n) return n < o.n;
+        for (int k = 0; k < 12; ++k)
+            if (p[k] != o.p[k]) return p[k] < o.p[k];
+        return false;
+    }
+};
+
+struct GraphEntry {
+    hipGraphExec_t exec;
+    uint64_t last_use;
+};
+
+constexpr size_t kGraphCache = 16;
+std::mutex g_graph_mu;
+std::map<GraphKey, GraphEntry> g_graphs;
+uint64_t g_graph_clock = 0;
+std::map<int, hipStream_t> g_capture_streams;
+
+// Finds or builds the graph for `sv`; returns it through `exec`.
+int32_t graph_for(const Solve &sv, int dev, const void *ws, hipGraphExec_t *exec) {
+    GraphKey key{dev, sv.order, sv.qkind, sv.qbits, sv.m, sv.n,
+                 {sv.W, sv.LA, sv.LB, sv.codes, sv.scales, sv.zeros, sv.V, sv.E, sv.sum_e2,
+                  sv.dev_status, ws, nullptr}};
+    std::lock_guard<std::mutex> lock(g_graph_mu);
+    auto it = g_graphs.find(key);
+    if (it != g_graphs.end()) {
+        it->second.last_use = ++g_graph_clock;
+        *exec = it->second.exec;
+        return BAKRON_OK;
+    }
+    hipStream_t cs;
+    auto cit = g_capture_streams.find(dev);
+    if (cit == g_capture_streams.end()) {
+        BK_HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+        g_capture_streams[dev] = cs;
+    } else {
+        cs = cit->second;
+    }
+    BK_HIP_CHECK(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+    int32_t st = enqueue_solve(sv, cs, nullptr, nullptr);
+    hipGraph_t graph = nullptr;
+    hipError_t ce = hipStreamEndCapture(cs, &graph);
+    if (st != BAKRON_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return st;
+    }
+    if (ce != hipSuccess) {
+        set_error("hipStreamEndCapture: %s", hipGetErrorString(ce));
+        return BAKRON_ERR_HIP;
+    }
+    hipGraphExec_t ge;
+    hipError_t ie = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ie != hipSuccess) {
+        set_error("hipGraphInstantiate: %s", hipGetErrorString(ie));
+        return BAKRON_ERR_HIP;
+    }
+    if (g_graphs.size() >= kGraphCache) {
+        auto victim = g_graphs.begin();
+        for (auto jt = g_graphs.begin(); jt != g_graphs.end(); ++jt)
+            if (jt->second.last_use < victim->second.last_use) victim = jt;
+        (void)hipGraphExecDestroy(victim->second.exec);
+        g_graphs.erase(victim);
+    }
+    g_graphs[key] = GraphEntry{ge, ++g_graph_clock};
+    *exec = ge;
+    return BAKRON_OK;
+}
+
+}  // namespace
+}  // namespace bakron
+
 extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
                                    const float *LB, int32_t qkind, int32_t qbits, int8_t *codes,
                                    float *scales, float *zeros, float *V, float *E,
@@ -869,7 +1057,7 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     BK_REQUIRE(m >= 1 && n >= 1 && m <= MAX_DIM && n <= MAX_DIM, "bad shape %lld x %lld",
                (long long)m, (long long)n);
     BK_REQUIRE(valid_quantizer(qkind, qbits), "unsupported quantizer kind=%d bits=%d", qkind, qbits);
-    BK_REQUIRE((flags & ~(BAKRON_ORDER_MASK | BAKRON_FLAG_PHASE_TIMING)) == 0 &&
+    BK_REQUIRE((flags & ~(BAKRON_ORDER_MASK | BAKRON_FLAG_PHASE_TIMING | BAKRON_FLAG_NO_GRAPH)) == 0 &&
                    (flags & BAKRON_ORDER_MASK) != 3,
                "unknown flags 0x%x", flags);
     const size_t need = bakron_quantize_workspace_size(m, n, qkind, qbits);
@@ -882,131 +1070,55 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     if (st != BAKRON_OK) return st;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    const int64_t mp = round_up(m, TB), np = round_up(n, TB);
-    const int M = (int)(mp / TB), N = (int)(np / TB);
-    const ShapeInfo &si = shape_info(M, N);
-    int order = flags & BAKRON_ORDER_MASK;
-    if (order == BAKRON_ORDER_AUTO) order = si.auto_order;
-    Buffers b;
-    carve(ws, mp, np, &b);
+    Solve sv{};
+    sv.W = W; sv.LA = LA; sv.LB = LB; sv.m = m; sv.n = n;
+    sv.mp = round_up(m, TB);
+    sv.np = round_up(n, TB);
+    sv.M = (int)(sv.mp / TB);
+    sv.N = (int)(sv.np / TB);
+    const ShapeInfo &si = shape_info(sv.M, sv.N);
+    sv.order = flags & BAKRON_ORDER_MASK;
+    if (sv.order == BAKRON_ORDER_AUTO) sv.order = si.auto_order;
+    sv.qkind = qkind;
+    sv.qbits = qbits;
+    if (qkind == BAKRON_Q_SYM) { sv.qmin = -(1 << (qbits - 1)); sv.qmax = (1 << (qbits - 1)) - 1; }
+    else if (qkind == BAKRON_Q_ASYM) { sv.qmin = 0; sv.qmax = (1 << qbits) - 1; }
+    else { sv.qmin = -128; sv.qmax = 127; }
+    sv.codes = codes; sv.scales = scales; sv.zeros = zeros; sv.V = V; sv.E = E;
+    sv.sum_e2 = sum_e2; sv.dev_status = dev_status;
+    carve(ws, sv.mp, sv.np, &sv.b);
 
-    int qmin, qmax;
-    if (qkind == BAKRON_Q_SYM) { qmin = -(1 << (qbits - 1)); qmax = (1 << (qbits - 1)) - 1; }
-    else if (qkind == BAKRON_Q_ASYM) { qmin = 0; qmax = (1 << qbits) - 1; }
-    else { qmin = -128; qmax = 127; }
-
-    const bool timing = (flags & BAKRON_FLAG_PHASE_TIMING) != 0;
-    std::vector<hipEvent_t> evs;
-    std::vector<int> ev_phase;
-    auto mark = [&](int phase) -> int32_t {
-        if (!timing) return BAKRON_OK;
-        hipEvent_t e;
-        BK_HIP_CHECK(hipEventCreate(&e));
-        BK_HIP_CHECK(hipEventRecord(e, stream));
-        evs.push_back(e);
-        ev_phase.push_back(phase);
-        return BAKRON_OK;
-    };
-    auto release = [&]() {
-        for (hipEvent_t e : evs) (void)hipEventDestroy(e);
-    };
-#define BK_MARK(p)                        \
-    do {                                  \
-        int32_t s_ = mark(p);             \
-        if (s_ != BAKRON_OK) {            \
-            release();                    \
-            return s_;                    \
-        }                                 \
-    } while (0)
-#define BK_LAUNCHED(what)                                                                  \
-    do {                                                                                   \
-        hipError_t e_ = hipGetLastError();                                                 \
-        if (e_ != hipSuccess) {                                                            \
-            set_error("launch of %s failed: %s", what, hipGetErrorString(e_));             \
-            release();                                                                     \
-            return BAKRON_ERR_HIP;                                                         \
-        }                                                                                  \
-    } while (0)
-
-    // phase 0: quantizer parameters + relayout
-    BK_MARK(-1);
-    hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, W, m, n, qkind,
-                       qbits, scales, zeros, b.sc, b.zp, dev_status);
-    BK_LAUNCHED("qparams_kernel");
-    const unsigned rl_blocks = 256u * 8u;
-    const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0);
-    const int a_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(LA) & 15) == 0);
-    const int b_vec = (m % 4 == 0) && ((reinterpret_cast<uintptr_t>(LB) & 15) == 0);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, W, m, n, b.Wp, mp,
-                       np, 0, w_vec);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LA, n, n, b.LAp,
-                       np, np, 1, a_vec);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LB, m, m, b.LBp,
-                       mp, mp, 1, b_vec);
-    BK_LAUNCHED("relayout_kernel");
-    BK_MARK(0);
-
-    LeafArgs la{b.Wp, b.Ebuf, b.LAp, b.LBp, b.sc, b.zp, mp, np, M, N, order, qmin, qmax,
-                codes, V, E, m, n, dev_status};
-    std::vector<Node> nodes;
-    nodes.reserve(2 * (M + N));
-    build_nodes(0, M + N - 1, nodes);
-    for (const Node &nd : nodes) {
-        if (nd.leaf) {
-            const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
-            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(256), 0, stream, la, nd.K);
-            BK_LAUNCHED("leaf_kernel");
-            BK_MARK(1);
-        } else {
-            Launch p1, p2;
-            band_launches(order, nd.K, nd.L, nd.H, M, N, p1, p2);
-            BandArgs g1{}, g2{};
-            if (order == BAKRON_ORDER_LA_FIRST) {
-                g1 = BandArgs{b.LAp, b.Ebuf, b.Tbuf, np, np, mp, 0, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
-                g2 = BandArgs{b.LBp, b.Tbuf, b.Wp, mp, mp, np, 1, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
+    if (flags & BAKRON_FLAG_PHASE_TIMING) {
+        std::vector<hipEvent_t> evs;
+        std::vector<int> ev_phase;
+        st = enqueue_solve(sv, stream, &evs, &ev_phase);
+        if (st == BAKRON_OK) {
+            hipError_t e = hipEventSynchronize(evs.back());
+            if (e != hipSuccess) {
+                set_error("hipEventSynchronize: %s", hipGetErrorString(e));
+                st = BAKRON_ERR_HIP;
             } else {
-                g1 = BandArgs{b.LBp, b.Ebuf, b.Tbuf, mp, mp, np, 2, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
-                g2 = BandArgs{b.Tbuf, b.LAp, b.Wp, np, np, np, 3, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
+                for (int k = 0; k < 6; ++k) g_phase_ms[k] = 0.0;
+                for (size_t k = 1; k < evs.size(); ++k) {
+                    float ms = 0.0f;
+                    (void)hipEventElapsedTime(&ms, evs[k - 1], evs[k]);
+                    const int ph = ev_phase[k];
+                    g_phase_ms[ph] += ms;
+                    if (ph == 1) g_phase_ms[4] += 1;
+                    if (ph == 2) g_phase_ms[5] += 2;
+                }
+                g_phase_valid = true;
             }
-            if (p1.rows > 0) {
-                hipLaunchKernelGGL(band_gemm_kernel, dim3(p1.cols, p1.rows), dim3(256), 0, stream, g1);
-                BK_LAUNCHED("band_gemm_kernel");
-            }
-            if (p2.rows > 0) {
-                hipLaunchKernelGGL(band_gemm_kernel, dim3(p2.cols, p2.rows), dim3(256), 0, stream, g2);
-                BK_LAUNCHED("band_gemm_kernel");
-            }
-            BK_MARK(2);
         }
+        for (hipEvent_t e : evs) (void)hipEventDestroy(e);
+        return st;
     }
-    if (sum_e2) {
-        hipLaunchKernelGGL(sumsq_partial_kernel, dim3(NPART), dim3(256), 0, stream, b.Ebuf,
-                           mp * np, b.partial);
-        hipLaunchKernelGGL(sumsq_final_kernel, dim3(1), dim3(256), 0, stream, b.partial, sum_e2);
-        BK_LAUNCHED("sumsq kernels");
-    }
-    BK_MARK(3);
-
-    if (timing) {
-        hipError_t e = hipEventSynchronize(evs.back());
-        if (e != hipSuccess) {
-            set_error("hipEventSynchronize: %s", hipGetErrorString(e));
-            release();
-            return BAKRON_ERR_HIP;
-        }
-        for (int k = 0; k < 6; ++k) g_phase_ms[k] = 0.0;
-        for (size_t k = 1; k < evs.size(); ++k) {
-            float ms = 0.0f;
-            (void)hipEventElapsedTime(&ms, evs[k - 1], evs[k]);
-            const int ph = ev_phase[k];
-            g_phase_ms[ph] += ms;
-            if (ph == 1) g_phase_ms[4] += 1;
-            if (ph == 2) g_phase_ms[5] += 2;
-        }
-        g_phase_valid = true;
-        release();
-    }
-#undef BK_MARK
-#undef BK_LAUNCHED
+    if (flags & BAKRON_FLAG_NO_GRAPH) return enqueue_solve(sv, stream, nullptr, nullptr);
+    int dev = 0;
+    BK_HIP_CHECK(hipGetDevice(&dev));
+    hipGraphExec_t exec;
+    st = graph_for(sv, dev, ws, &exec);
+    if (st != BAKRON_OK) return st;
+    BK_HIP_CHECK(hipGraphLaunch(exec, stream));
     return BAKRON_OK;
 }
