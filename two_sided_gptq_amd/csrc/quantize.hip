@@ -174,301 +174,309 @@ __device__ inline float dot4(const float4 a, const float4 b, float s) {
 //   Z[r][c] = sum_{k <= c} E[r][k] LA[c][k]                  (row direction)
 //   P[r][c] = W[r][c] - LB[r][r] sum_{k < c} E[r][k] LA[c][k]
 //                     - sum_{k < r} LB[r][k] Z[k][c]         (column direction)
-// Step d rounds the in-tile anti-diagonal r + c = d.  Each entry is handled by
-// a group of 4 lanes: lane q takes the float4 chunks 4j + q (j = 0..3) of the
-// two length-64 dot products; a 2-step DPP butterfly gives all 4 lanes the
-// sums and every lane of the group rounds (no broadcast needed).
+// Step d rounds the in-tile anti-diagonal r + c = d (127 steps).
 //
-// Only two terms of an entry's dots come from the step just before it:
-// E[r][c-1] LA[c][c-1] and LB[r][r-1] Z[r-1][c].  Everything else is at least
-// two steps old, so the operands of both dots for step d+1 are loaded during
-// step d (double-buffered registers) and summed at the start of step d+1
-// while the one fresh neighbour value is in flight:
-//   steps 0..63:   group g owns row g (its LB row is kept in registers with
-//                  element g-1 zeroed; the fresh Z[g-1][c] is read after the
-//                  barrier; its own E[g][c-1] is still in a register);
-//   steps 64..126: group g owns column 63-g (its LA row in registers with
-//                  element c-1 zeroed; fresh E[r][c-1] read after the
-//                  barrier; its own Z[r-1][c] still in a register).
-// A load of the group's own row/column never sees the value the group writes
-// later in the same step (LDS operations of one wave complete in order), and
-// the value a neighbouring group may be writing meanwhile is multiplied by
-// the zeroed register element.  E and Z start at zero and the factors are
-// lower triangular, so 16-wide chunks beyond a wave's largest column (first
-// dot) or row (second dot) are exact zeros and are not loaded.  Those chunk
-// counts depend only on the wave and on a 16-step segment of d, so each
-// (wave, segment) pair is its own template instance: every LDS wait count is
-// static and the critical read never waits for the operand loads behind it.
-// Rows of the LDS tiles are 80 floats apart, so four consecutive rows occupy
-// disjoint 64-byte bank groups.
-constexpr int LQ = LP / 4;  // LDS row stride in float4
+// Wave 0 is the chain: lane r owns row r for the whole sweep (it is active at
+// steps r .. r+63) and rounds entry (r, d - r) at step d.  The two dots are
+// split at a boundary s0 that moves every LJ steps: terms produced before
+// step s0 (the bulk) come precomputed from the three helper waves, the rest
+// (the last LJ..2LJ-1 terms of each dot) the chain adds itself:
+//   row direction     its own last errors E[r][c-j], kept in registers;
+//   column direction  Z[r-j][c], which lane r-j produced j steps ago.  Lane r
+//                     keeps those in a delay line that is shifted down one
+//                     lane per step with a whole-wave DPP shift, so the value
+//                     just produced by the lane above arrives without LDS or
+//                     a barrier.
+// The chain and the helpers meet at a workgroup barrier once every LJ steps:
+// during block t (steps LJ t .. LJ t + LJ - 1) the helpers compute the bulk
+// of block t+1 from the E and Z values of steps < LJ t, which the previous
+// barrier made visible, into the other half of a double buffer.  A helper
+// unit is one row r (row-direction bulk of its LJ entries in the block, which
+// share E[r][0..]) or one column c (column-direction bulk of its LJ entries,
+// which share Z[0..][c]); 4 lanes split each dot into float4 chunks and a DPP
+// butterfly sums them.  Values the chain may be writing concurrently are never
+// used: the operand is masked to the bulk's length before multiplying.
+constexpr int LJ = 4;                               // chain steps per block
+constexpr int LWIN = 2 * LJ - 1;                    // most recent terms per dot
+constexpr int NBLK = (2 * TB - 1 + LJ - 1) / LJ;    // blocks covering the sweep
+constexpr int NSTEP = NBLK * LJ;                    // steps including the idle tail
+constexpr int LEAF_THREADS = 512;                   // 8 waves, two per SIMD
+constexpr int NHELP = 384;                          // helper lanes: waves 1-3 and 5-7
+// wave 0 is the chain; wave 4 (on the chain's SIMD) only takes part in the
+// barriers, so the chain has its SIMD to itself
+constexpr int WSP = NSTEP + 4;                      // row stride of the skewed W copy
+constexpr int CX = TB;                              // index of column 0 in the padded LA tables
+constexpr int NCX = CX + NSTEP + 4;                 // padded LA table length (columns -64 .. 131)
+static_assert(LWIN <= 7, "the LA band holds sub-diagonals 1..7");
+static_assert(WSP % 4 == 0 && LJ == 4, "one float4 of W per block; 4-lane helper groups");
+static_assert(NBLK % 2 == 0, "the chain alternates two operand buffers");
 
-__shared__ __align__(16) float lf_W[TB * LP];
+__shared__ __align__(16) float lf_Wk[TB * WSP];  // lf_Wk[r][d] = W[r][d - r] (row r skewed by r)
 __shared__ __align__(16) float lf_E[TB * LP];
-__shared__ __align__(16) float lf_Z[TB * LP];  // lf_Z[c][k] = Z[k][c]
-__shared__ __align__(16) float lf_B[TB * LP];  // LB[I,I]
-__shared__ __align__(16) float lf_A[TB * LP];  // LA[J,J]
-__shared__ float4 lf_row[TB];                  // (s, 1/s, z, 1/LB_rr)
-__shared__ float2 lf_col[TB];                  // (LA_cc, 1/LA_cc)
-__shared__ int8_t lf_C[TB * TB];
+__shared__ __align__(16) float lf_Z[TB * LP];    // lf_Z[c][k] = Z[k][c]
+__shared__ __align__(16) float lf_B[TB * LP];    // LB[I,I]
+__shared__ __align__(16) float lf_A[TB * LP];    // LA[J,J]
+__shared__ float4 lf_Ab[NCX * 2];                // CX + c: LA[c][c], LA[c][c-1 .. c-7]; 0 off 0..63
+__shared__ float lf_ila[NCX];                    // CX + c: 1 / LA_cc; 0 off 0..63
+__shared__ float4 lf_row[TB];                    // (s, 1/s, z, 1/LB_rr)
+__shared__ __align__(16) float lf_bulk[2 * 2 * TB * LJ];  // [buffer][direction][row][step in block]
+__shared__ float lf_sink[3 * TB];                // write targets of idle lanes
+__shared__ int8_t lf_C[TB * TB + TB];            // codes, then one sink byte per lane
 
-struct Bulk {
-    float4 x[4], y[4], z[4];
+// the value lane l-1 holds, in lane l (lane 0 gets 0): a whole-wave shift
+__device__ __forceinline__ float from_lane_above(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x138, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ int clamp_col(int c) { return min(max(c, 0), TB - 1); }
+
+// wave 0; lane r = row r.  Every per-step LDS address is linear in the step d:
+// W is stored skewed, the LA tables are padded over every column the lane
+// passes, and idle lanes write to their own sink words.  The constant
+// operands of block t+1 are loaded while block t runs.
+struct ChainBlock {
+    float4 w4;           // W[r][d - r] for the block's LJ steps
+    float4 a[LJ][2];     // LA band of each step's column
+    float ila[LJ];       // 1 / LA_cc of each step's column
 };
 
-struct Lane {
-    int g, q;
+__device__ __forceinline__ void chain_load(ChainBlock &cb, const float *wrow, const float4 *ab,
+                                           const float *ib, int t) {
+    cb.w4 = *reinterpret_cast<const float4 *>(wrow + LJ * t);
+#pragma unroll
+    for (int p = 0; p < LJ; ++p) {
+        const int d = LJ * t + p;
+        cb.a[p][0] = ab[2 * d];
+        cb.a[p][1] = ab[2 * d + 1];
+        cb.ila[p] = ib[d];
+    }
+}
+
+struct ChainState {
+    float lbb[LWIN + 1];   // LB[r][r - j]
+    float4 rc;             // (s, 1/s, z, 1/LB_rr)
     float qminf, qmaxf;
-    int bad;
+    float eh[LWIN], zl[LWIN];  // eh[j] = E[r][c-1-j], zl[j] = Z[r-1-j][c]
+    int r, e_off, z_off, c_off;
 };
 
-__device__ __forceinline__ float4 f4(int i, const float *base) {
-    return reinterpret_cast<const float4 *>(base)[i];
-}
-
-// zero component t of a float4 (t in 0..3; any other value leaves it)
-__device__ inline float4 zero_component(float4 v, int t) {
-    v.x = t == 0 ? 0.0f : v.x;
-    v.y = t == 1 ? 0.0f : v.y;
-    v.z = t == 2 ? 0.0f : v.z;
-    v.w = t == 3 ? 0.0f : v.w;
-    return v;
-}
-
-// round entry (r, c) given its dot products; writes E, Z and the code; returns e
-__device__ __forceinline__ float leaf_round(Lane &L, int r, int c, float wv, float lbd, float d1,
-                                            float d2, float4 rc, float2 cc, float &zv) {
-    const float P = wv - lbd * d1 - d2;
-    const float cz = fminf(fmaxf(rintf(P * rc.y) + rc.z, L.qminf), L.qmaxf);
-    const float v = rc.x * (cz - rc.z);
-    const float e = (P - v) * (rc.w * cc.y);
-    zv = fmaf(e, cc.x, d1);
-    L.bad |= !isfinite(e);
-    if (L.q == 0) {
-        lf_E[r * LP + c] = e;
-        lf_Z[c * LP + r] = zv;
-        lf_C[r * TB + c] = (int8_t)(int)cz;
+__device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb, int t) {
+    const int r = st.r;
+    float bulk1[LJ], bulk2[LJ];
+#pragma unroll
+    for (int p = 0; p < LJ; ++p) {
+        bulk1[p] = lf_bulk[(((t & 1) * 2 + 0) * TB + r) * LJ + p];
+        bulk2[p] = lf_bulk[(((t & 1) * 2 + 1) * TB + r) * LJ + p];
     }
-    return e;
-}
-
-// steps 0..63: group g owns row r = g.  Loads the operands for step d + 1 into
-// nxt; with COMPUTE, rounds this step's entry from cur.
-template <int NJ1, int NJ2, bool COMPUTE>
-__device__ __forceinline__ void p1_step(Lane &L, int d, const float4 (&lbm)[4], float lb_last,
-                                        float lbd, float4 rc, float &e_prev, Bulk &cur,
-                                        Bulk &nxt) {
-    const int r = L.g, q = L.q;
-    const bool act = COMPUTE && r <= d;
-    const int c = act ? d - r : 0;
-    float zc = 0.0f, wv = 0.0f, la_last = 0.0f;
-    float2 cc = make_float2(1.0f, 1.0f);
-    if (COMPUTE) {
-        zc = lf_Z[c * LP + max(r - 1, 0)];
-        wv = lf_W[r * LP + c];
-        cc = lf_col[c];
-        la_last = lf_A[c * LP + max(c - 1, 0)];
-    }
-    // keep the fresh read ahead of the operand loads in the in-order LDS queue
-    __builtin_amdgcn_sched_barrier(0);
-    const int cn = min(max(d + 1 - r, 0), TB - 1);
+    const float wv[4] = {cb.w4.x, cb.w4.y, cb.w4.z, cb.w4.w};
 #pragma unroll
-    for (int j = 0; j < NJ1; ++j) {
-        nxt.x[j] = f4(r * LQ + 4 * j + q, lf_E);
-        nxt.y[j] = f4(cn * LQ + 4 * j + q, lf_A);
-    }
-    if (NJ1 < 4) nxt.x[NJ1 < 4 ? NJ1 : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < LJ; ++p) {
+        const int d = LJ * t + p;
+        const float la[8] = {cb.a[p][0].x, cb.a[p][0].y, cb.a[p][0].z, cb.a[p][0].w,
+                             cb.a[p][1].x, cb.a[p][1].y, cb.a[p][1].z, cb.a[p][1].w};
+        // recent terms j = 2 .. LJ + p (steps s0 .. d-2), then the fresh j = 1
+        float y = 0.0f, s2 = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NJ2; ++j) nxt.z[j] = f4(cn * LQ + 4 * j + q, lf_Z);
-    if (COMPUTE) {
-        float n1 = 0.0f, n2 = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NJ1; ++j) n1 = dot4(cur.x[j], cur.y[j], n1);
-#pragma unroll
-        for (int j = 0; j < NJ2; ++j) n2 = dot4(lbm[j], cur.z[j], n2);
-        const float b1 = group4_sum(n1), b2 = group4_sum(n2);
-        if (act) {
-            float zv;
-            e_prev = leaf_round(L, r, c, wv, lbd, fmaf(e_prev, la_last, b1), fmaf(lb_last, zc, b2),
-                                rc, cc, zv);
+        for (int j = LJ + p; j >= 2; --j) {
+            y = fmaf(st.eh[j - 1], la[j], y);
+            s2 = fmaf(st.lbb[j], st.zl[j - 1], s2);
         }
-    }
-    __syncthreads();
-}
-
-template <int W, int S>
-__device__ __forceinline__ void p1_segment(Lane &L, const float4 (&lbm)[4], float lb_last,
-                                           float lbd, float4 rc, float &e_prev, Bulk &A, Bulk &B) {
-    constexpr int d0 = 16 * S;
-    if constexpr (S + 1 < W) {
-        for (int i = 0; i < 16; ++i) __syncthreads();
-    } else if constexpr (S + 1 == W) {
-        for (int i = 0; i < 15; ++i) __syncthreads();
-        p1_step<0, W + 1, false>(L, d0 + 15, lbm, lb_last, lbd, rc, e_prev, B, A);
-    } else {
-        constexpr int NJ1 = S - W + 1, NJ2 = W + 1;
-        for (int i = 0; i < 16; i += 2) {
-            p1_step<NJ1, NJ2, true>(L, d0 + i, lbm, lb_last, lbd, rc, e_prev, A, B);
-            p1_step<NJ1, NJ2, true>(L, d0 + i + 1, lbm, lb_last, lbd, rc, e_prev, B, A);
+        y += bulk1[p];
+        s2 += bulk2[p];
+        y = fmaf(st.eh[0], la[1], y);
+        s2 = fmaf(st.lbb[1], st.zl[0], s2);
+        const float P = wv[p] - fmaf(st.lbb[0], y, s2);
+        const float qz = fminf(fmaxf(rintf(P * st.rc.y) + st.rc.z, st.qminf), st.qmaxf);
+        const float v = st.rc.x * (qz - st.rc.z);
+        const bool act = (unsigned)(d - r) < (unsigned)TB;
+        float e = (P - v) * (st.rc.w * cb.ila[p]);
+        float z = fmaf(e, la[0], y);
+        *(act ? lf_E + st.e_off + d : lf_sink + r) = e;
+        *(act ? lf_Z + st.z_off + d * LP : lf_sink + TB + r) = z;
+        *(act ? lf_C + st.c_off + d : lf_C + TB * TB + r) = (int8_t)(int)qz;
+        e = act ? e : 0.0f;
+        z = act ? z : 0.0f;
+#pragma unroll
+        for (int j = LWIN - 1; j >= 1; --j) {
+            st.eh[j] = st.eh[j - 1];
+            st.zl[j] = from_lane_above(st.zl[j - 1]);
         }
+        st.eh[0] = e;
+        st.zl[0] = from_lane_above(z);
     }
-    if constexpr (S < 3) p1_segment<W, S + 1>(L, lbm, lb_last, lbd, rc, e_prev, A, B);
 }
 
-// steps 64..126: group g owns column c = 63 - g, row r = d - c
-template <int NJ1, int NJ2>
-__device__ __forceinline__ void p2_step(Lane &L, int d, bool wave_act, const float4 (&lam)[4],
-                                        float la_last, float2 cc, float &z_prev, Bulk &cur,
-                                        Bulk &nxt) {
-    const int c = TB - 1 - L.g, q = L.q;
-    if (wave_act) {
-        const bool act = L.g <= 2 * TB - 2 - d;
-        const int r = act ? d - c : TB - 1;
-        const float ec = lf_E[r * LP + max(c - 1, 0)];
-        const float wv = lf_W[r * LP + c];
-        const float4 rc = lf_row[r];
-        const float lbd = lf_B[r * LP + r];
-        const float lb_last = lf_B[r * LP + r - 1];
-        // keep the fresh read ahead of the operand loads in the in-order LDS queue
-        __builtin_amdgcn_sched_barrier(0);
-        const int rn = min(r + 1, TB - 1);
+__device__ __forceinline__ void leaf_chain(const int r, const float qminf, const float qmaxf) {
+    ChainState st;
+    st.r = r;
+    st.lbb[0] = lf_B[r * LP + r];
 #pragma unroll
-        for (int j = 0; j < NJ1; ++j) nxt.x[j] = f4(rn * LQ + 4 * j + q, lf_E);
+    for (int j = 1; j <= LWIN; ++j) st.lbb[j] = r >= j ? lf_B[r * LP + r - j] : 0.0f;
+    st.rc = lf_row[r];
+    st.qminf = qminf;
+    st.qmaxf = qmaxf;
 #pragma unroll
-        for (int j = 0; j < NJ2; ++j) {
-            nxt.y[j] = f4(rn * LQ + 4 * j + q, lf_B);
-            nxt.z[j] = f4(c * LQ + 4 * j + q, lf_Z);
+    for (int j = 0; j < LWIN; ++j) st.eh[j] = st.zl[j] = 0.0f;
+    st.e_off = r * (LP - 1);   // E[r][d - r]
+    st.z_off = -r * (LP - 1);  // Z^T[d - r][r] at z_off + d LP
+    st.c_off = r * (TB - 1);   // C[r][d - r]
+    const float *wrow = lf_Wk + r * WSP;
+    const float4 *ab = lf_Ab + 2 * (CX - r);  // step d: ab[2d], ab[2d + 1]
+    const float *ib = lf_ila + (CX - r);      // step d: ib[d]
+    ChainBlock c0, c1;
+    chain_load(c0, wrow, ab, ib, 0);
+    for (int t = 0; t < NBLK; t += 2) {
+        chain_load(c1, wrow, ab, ib, t + 1);
+        chain_block(st, c0, t);
+        __syncthreads();
+        chain_load(c0, wrow, ab, ib, t + 2);
+        chain_block(st, c1, t + 1);
+        __syncthreads();
+    }
+}
+
+// One helper unit: 4 lanes (q = 0..3) compute the LJ bulk dots of one row
+// (dir 0, row direction, X = E[idx][.], Y = LA rows of the entries' columns) or
+// one column (dir 1, column direction, X = Z[.][idx], Y = LB rows of the
+// entries' rows) over k < len; lane q then holds entry q's total and writes it.
+__device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float *buf, int q) {
+    const int idx = lo + (u >> 1), dir = u & 1;
+    const int len = s0 - idx;
+    const float *X = (dir ? lf_Z : lf_E) + idx * LP + 4 * q;
+    const float *Yb = (dir ? lf_B : lf_A) + 4 * q;
+    const float *Y[LJ];
+    float acc[LJ];
+#pragma unroll
+    for (int p = 0; p < LJ; ++p) {
+        Y[p] = Yb + clamp_col(D0 + p - idx) * LP;
+        acc[p] = 0.0f;
+    }
+    const int nfull = len > 0 ? len >> 4 : 0;
+    if (nfull > 0) {
+        float4 x = *reinterpret_cast<const float4 *>(X);
+        float4 y[LJ];
+#pragma unroll
+        for (int p = 0; p < LJ; ++p) y[p] = *reinterpret_cast<const float4 *>(Y[p]);
+        for (int ch = 1; ch < nfull; ++ch) {
+            const float4 xn = *reinterpret_cast<const float4 *>(X + 16 * ch);
+            float4 yn[LJ];
+#pragma unroll
+            for (int p = 0; p < LJ; ++p) yn[p] = *reinterpret_cast<const float4 *>(Y[p] + 16 * ch);
+#pragma unroll
+            for (int p = 0; p < LJ; ++p) acc[p] = dot4(x, y[p], acc[p]);
+            x = xn;
+#pragma unroll
+            for (int p = 0; p < LJ; ++p) y[p] = yn[p];
         }
-        if (NJ2 < 4) nxt.y[NJ2 < 4 ? NJ2 : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
-        float n1 = 0.0f, n2 = 0.0f;
 #pragma unroll
-        for (int j = 0; j < NJ1; ++j) n1 = dot4(cur.x[j], lam[j], n1);
+        for (int p = 0; p < LJ; ++p) acc[p] = dot4(x, y[p], acc[p]);
+    }
+    if (len > 0 && (len & 15) != 0) {
+        // tail chunk: elements at or beyond len may be in flux; mask them
+        const int k0 = 16 * nfull + 4 * q;
+        float4 x = *reinterpret_cast<const float4 *>(X + 16 * nfull);
+        x.x = k0 < len ? x.x : 0.0f;
+        x.y = k0 + 1 < len ? x.y : 0.0f;
+        x.z = k0 + 2 < len ? x.z : 0.0f;
+        x.w = k0 + 3 < len ? x.w : 0.0f;
 #pragma unroll
-        for (int j = 0; j < NJ2; ++j) n2 = dot4(cur.y[j], cur.z[j], n2);
-        const float b1 = group4_sum(n1), b2 = group4_sum(n2);
-        if (act) {
-            float zv;
-            leaf_round(L, r, c, wv, lbd, fmaf(ec, la_last, b1), fmaf(lb_last, z_prev, b2), rc, cc,
-                       zv);
-            z_prev = zv;
+        for (int p = 0; p < LJ; ++p)
+            acc[p] = dot4(x, *reinterpret_cast<const float4 *>(Y[p] + 16 * nfull), acc[p]);
+    }
+    // 4 x 4 transpose-reduce over the group: lane q ends with entry q's sum
+    const bool o1 = q & 1, o2 = q & 2;
+    const float k0v = o1 ? acc[1] : acc[0], s0v = o1 ? acc[0] : acc[1];
+    const float k1v = o1 ? acc[3] : acc[2], s1v = o1 ? acc[2] : acc[3];
+    const float r0 = k0v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0v), 0xB1, 0xF, 0xF, false));
+    const float r1 = k1v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1v), 0xB1, 0xF, 0xF, false));
+    const float kv = o2 ? r1 : r0, sv = o2 ? r0 : r1;
+    const float tot = kv + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sv), 0x4E, 0xF, 0xF, false));
+    const int other = D0 + q - idx;
+    float *dst = (other >= 0 && other < TB) ? buf + (dir * TB + (dir ? other : idx)) * LJ + q
+                                            : lf_sink + 2 * TB + (threadIdx.x & 63);
+    *dst = tot;
+}
+
+// helper waves; hl = helper lane 0..NHELP-1, groups of 4 lanes
+__device__ __forceinline__ void leaf_helpers(const int hl) {
+    const int g = hl >> 2, q = hl & 3;
+    constexpr int NG = NHELP / 4;
+    for (int t = 0; t < NBLK; ++t) {
+        if (t + 1 < NBLK) {
+            // bulk of block t+1: diagonals D0 .. D0+LJ-1, terms of steps < s0
+            const int D0 = LJ * (t + 1), s0 = LJ * t;
+            const int lo = max(0, D0 - (TB - 1)), hi = min(TB - 1, D0 + LJ - 1);
+            const int nunit = 2 * (hi - lo + 1);
+            float *buf = lf_bulk + ((t + 1) & 1) * 2 * TB * LJ;
+            // units in order of decreasing length, dealt out in a snake
+            static_assert(2 * NG >= 2 * TB, "two unit slots per group cover every unit");
+            if (g < nunit) helper_unit(g, lo, D0, s0, buf, q);
+            if (2 * NG - 1 - g < nunit) helper_unit(2 * NG - 1 - g, lo, D0, s0, buf, q);
         }
-    }
-    __syncthreads();
-}
-
-template <int W, int K>
-__device__ __forceinline__ void p2_segment(Lane &L, const float4 (&lam)[4], float la_last,
-                                           float2 cc, float &z_prev, Bulk &A, Bulk &B) {
-    constexpr int t0 = 16 * K;
-    constexpr int len = K < 3 ? 16 : 15;
-    constexpr int NJ1 = 4 - W;
-    constexpr int NJ2 = (W + 2 + K < 4) ? (W + 2 + K) : 4;
-    constexpr int last = 62 - 16 * W;  // last active t of this wave
-    for (int i = 0; i + 1 < len; i += 2) {
-        p2_step<NJ1, NJ2>(L, TB + t0 + i, t0 + i <= last, lam, la_last, cc, z_prev, A, B);
-        p2_step<NJ1, NJ2>(L, TB + t0 + i + 1, t0 + i + 1 <= last, lam, la_last, cc, z_prev, B, A);
-    }
-    if constexpr (len & 1)
-        p2_step<NJ1, NJ2>(L, TB + t0 + len - 1, t0 + len - 1 <= last, lam, la_last, cc, z_prev, A, B);
-    if constexpr (K < 3) p2_segment<W, K + 1>(L, lam, la_last, cc, z_prev, A, B);
-}
-
-template <int W>
-__device__ __forceinline__ void leaf_sweep(Lane &L) {
-    const int g = L.g, q = L.q;
-    Bulk A, B;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        A.x[j] = A.y[j] = A.z[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        B.x[j] = B.y[j] = B.z[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    {   // steps 0..63
-        const int r = g;
-        float4 lbm[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            lbm[j] = zero_component(f4(r * LQ + 4 * j + q, lf_B),
-                                    (r >= 1 && (((r - 1) >> 4) == j) && ((((r - 1) >> 2) & 3) == q))
-                                        ? ((r - 1) & 3) : 4);
-        const float lb_last = r >= 1 ? lf_B[r * LP + r - 1] : 0.0f;
-        const float lbd = lf_B[r * LP + r];
-        const float4 rc = lf_row[r];
-        float e_prev = 0.0f;
-        p1_segment<W, 0>(L, lbm, lb_last, lbd, rc, e_prev, A, B);
-    }
-    {   // steps 64..126
-        const int c = TB - 1 - g;
-        float4 lam[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            lam[j] = zero_component(f4(c * LQ + 4 * j + q, lf_A),
-                                    (c >= 1 && (((c - 1) >> 4) == j) && ((((c - 1) >> 2) & 3) == q))
-                                        ? ((c - 1) & 3) : 4);
-        const float la_last = c >= 1 ? lf_A[c * LP + c - 1] : 0.0f;
-        const float2 cc = lf_col[c];
-        // operands for step 64: entry (g + 1, c), every E and Z so far is visible
-        const int rp = min(g + 1, TB - 1);
-        constexpr int NJ1 = 4 - W, NJ2 = W + 1;
-#pragma unroll
-        for (int j = 0; j < NJ1; ++j) A.x[j] = f4(rp * LQ + 4 * j + q, lf_E);
-#pragma unroll
-        for (int j = 0; j < NJ2; ++j) {
-            A.y[j] = f4(rp * LQ + 4 * j + q, lf_B);
-            A.z[j] = f4(c * LQ + 4 * j + q, lf_Z);
-        }
-        if (NJ2 < 4) A.y[NJ2 < 4 ? NJ2 : 0] = make_float4(0.f, 0.f, 0.f, 0.f);
-        float z_prev = 0.0f;  // the prologue's operands already include Z[g][c]
-        p2_segment<W, 0>(L, lam, la_last, cc, z_prev, A, B);
+        __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(256) void leaf_kernel(LeafArgs a, int K) {
+// the wave that shares the chain's SIMD: barriers only
+__device__ __forceinline__ void leaf_idle() {
+    for (int t = 0; t < NBLK; ++t) __syncthreads();
+}
+
+__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K) {
     const int tid = threadIdx.x;
     const int Ilo = max(0, K - a.N + 1);
     const int I = Ilo + blockIdx.x;
     const int J = K - I;
     const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
 
-    for (int idx = tid; idx < TB * 16; idx += 256) {
+    for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
         const int r = idx >> 4, c4 = (idx & 15) * 4;
-        *reinterpret_cast<float4 *>(lf_W + r * LP + c4) =
-            *reinterpret_cast<const float4 *>(a.Wp + (r0 + r) * a.np + c0 + c4);
+        const float4 wv = *reinterpret_cast<const float4 *>(a.Wp + (r0 + r) * a.np + c0 + c4);
+        float *wk = lf_Wk + r * WSP + r + c4;
+        wk[0] = wv.x;
+        wk[1] = wv.y;
+        wk[2] = wv.z;
+        wk[3] = wv.w;
         *reinterpret_cast<float4 *>(lf_B + r * LP + c4) =
             *reinterpret_cast<const float4 *>(a.LBp + (r0 + r) * a.mp + r0 + c4);
         *reinterpret_cast<float4 *>(lf_A + r * LP + c4) =
             *reinterpret_cast<const float4 *>(a.LAp + (c0 + r) * a.np + c0 + c4);
-        *reinterpret_cast<float4 *>(lf_E + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4 *>(lf_Z + r * LP + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    for (int idx = tid; idx < 2 * 2 * TB * LJ / 4; idx += LEAF_THREADS)
+        reinterpret_cast<float4 *>(lf_bulk)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
     if (tid < TB) {
         const float s = a.sc[r0 + tid];
         lf_row[tid] = make_float4(s, 1.0f / s, a.zp[r0 + tid], 1.0f / lf_B[tid * LP + tid]);
-        const float la = lf_A[tid * LP + tid];
-        lf_col[tid] = make_float2(la, 1.0f / la);
+    }
+    for (int x = tid; x < NCX; x += LEAF_THREADS) {
+        const int c = x - CX;
+        float band[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) band[j] = (c >= j && c < TB) ? lf_A[c * LP + c - j] : 0.0f;
+        lf_Ab[2 * x] = make_float4(band[0], band[1], band[2], band[3]);
+        lf_Ab[2 * x + 1] = make_float4(band[4], band[5], band[6], band[7]);
+        lf_ila[x] = band[0] != 0.0f ? 1.0f / band[0] : 0.0f;
     }
     __syncthreads();
 
-    Lane L{tid >> 2, tid & 3, (float)a.qmin, (float)a.qmax, 0};
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (w == 0) leaf_sweep<0>(L);
-    else if (w == 1) leaf_sweep<1>(L);
-    else if (w == 2) leaf_sweep<2>(L);
-    else leaf_sweep<3>(L);
+    if (w == 0) leaf_chain(tid, (float)a.qmin, (float)a.qmax);
+    else if (w == 4) leaf_idle();
+    else leaf_helpers(tid - (w < 4 ? 64 : 128));
     const float *Es = lf_E;
     const int8_t *Cs = lf_C;
     const float4 *s_row = lf_row;
-    const int bad = L.bad;
 
     // E tile to the band-update buffer
     if (a.order == BAKRON_ORDER_LA_FIRST) {
-        for (int idx = tid; idx < TB * 16; idx += 256) {
+        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
             const int r = idx >> 4, c4 = (idx & 15) * 4;
             *reinterpret_cast<float4 *>(a.Ebuf + (r0 + r) * a.np + c0 + c4) =
                 *reinterpret_cast<const float4 *>(Es + r * LP + c4);
         }
     } else {
-        for (int idx = tid; idx < TB * 16; idx += 256) {
+        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
             const int c = idx >> 4, rr4 = (idx & 15) * 4;
             *reinterpret_cast<float4 *>(a.Ebuf + (c0 + c) * a.mp + r0 + rr4) =
                 make_float4(Es[(rr4 + 0) * LP + c], Es[(rr4 + 1) * LP + c],
@@ -476,9 +484,11 @@ __global__ __launch_bounds__(256) void leaf_kernel(LeafArgs a, int K) {
         }
     }
     // caller-visible outputs
-    for (int idx = tid; idx < TB * TB; idx += 256) {
+    int bad = 0;
+    for (int idx = tid; idx < TB * TB; idx += LEAF_THREADS) {
         const int r = idx >> 6, c = idx & 63;
         const int64_t gi = r0 + r, gj = c0 + c;
+        bad |= !isfinite(Es[r * LP + c]);
         if (gi < a.m && gj < a.n) {
             const int8_t code = Cs[r * TB + c];
             a.codes[gi * a.n + gj] = code;
@@ -925,7 +935,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_
     for (const Node &nd : nodes) {
         if (nd.leaf) {
             const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
-            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(256), 0, stream, la, nd.K);
+            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream, la, nd.K);
             BK_LAUNCH_CHECK("leaf_kernel");
             BK_MARK(1);
         } else {
