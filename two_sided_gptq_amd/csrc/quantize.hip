@@ -200,10 +200,10 @@ constexpr int LJ = 4;                               // chain steps per block
 constexpr int LWIN = 2 * LJ - 1;                    // most recent terms per dot
 constexpr int NBLK = (2 * TB - 1 + LJ - 1) / LJ;    // blocks covering the sweep
 constexpr int NSTEP = NBLK * LJ;                    // steps including the idle tail
-constexpr int LEAF_THREADS = 512;                   // 8 waves, two per SIMD
-constexpr int NHELP = 384;                          // helper lanes: waves 1-3 and 5-7
-// wave 0 is the chain; wave 4 (on the chain's SIMD) only takes part in the
-// barriers, so the chain has its SIMD to itself
+constexpr int LEAF_THREADS = 768;                   // 12 waves, three per SIMD
+constexpr int NHELP = 576;                          // helper lanes: every wave not on SIMD 0
+// wave 0 is the chain; waves 4 and 8 (on the chain's SIMD) only take part in
+// the barriers, so the chain has its SIMD to itself
 constexpr int WSP = NSTEP + 4;                      // row stride of the skewed W copy
 constexpr int CX = TB;                              // index of column 0 in the padded LA tables
 constexpr int NCX = CX + NSTEP + 4;                 // padded LA table length (columns -64 .. 131)
@@ -211,7 +211,8 @@ static_assert(LWIN <= 7, "the LA band holds sub-diagonals 1..7");
 static_assert(WSP % 4 == 0 && LJ == 4, "one float4 of W per block; 4-lane helper groups");
 static_assert(NBLK % 2 == 0, "the chain alternates two operand buffers");
 
-__shared__ __align__(16) float lf_Wk[TB * WSP];  // lf_Wk[r][d] = W[r][d - r] (row r skewed by r)
+__shared__ __align__(16) float lf_Wk[TB * WSP];  // lf_Wk[r][d] = W[r][d - r] (row r skewed by r);
+                                                 // after step d the slot holds that entry's code
 __shared__ __align__(16) float lf_E[TB * LP];
 __shared__ __align__(16) float lf_Z[TB * LP];    // lf_Z[c][k] = Z[k][c]
 __shared__ __align__(16) float lf_B[TB * LP];    // LB[I,I]
@@ -221,7 +222,6 @@ __shared__ float lf_ila[NCX];                    // CX + c: 1 / LA_cc; 0 off 0..
 __shared__ float4 lf_row[TB];                    // (s, 1/s, z, 1/LB_rr)
 __shared__ __align__(16) float lf_bulk[2 * 2 * TB * LJ];  // [buffer][direction][row][step in block]
 __shared__ float lf_sink[3 * TB];                // write targets of idle lanes
-__shared__ int8_t lf_C[TB * TB + TB];            // codes, then one sink byte per lane
 
 // the value lane l-1 holds, in lane l (lane 0 gets 0): a whole-wave shift
 __device__ __forceinline__ float from_lane_above(float x) {
@@ -257,12 +257,14 @@ struct ChainState {
     float4 rc;             // (s, 1/s, z, 1/LB_rr)
     float qminf, qmaxf;
     float eh[LWIN], zl[LWIN];  // eh[j] = E[r][c-1-j], zl[j] = Z[r-1-j][c]
-    int r, e_off, z_off, c_off;
+    float *wrow;           // the lane's row of the skewed W copy; its consumed slots take the codes
+    int r, e_off, z_off;
 };
 
+template <bool ZP>
 __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb, int t) {
     const int r = st.r;
-    float bulk1[LJ], bulk2[LJ];
+    float bulk1[LJ], bulk2[LJ], code[LJ];
 #pragma unroll
     for (int p = 0; p < LJ; ++p) {
         bulk1[p] = lf_bulk[(((t & 1) * 2 + 0) * TB + r) * LJ + p];
@@ -286,14 +288,21 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
         y = fmaf(st.eh[0], la[1], y);
         s2 = fmaf(st.lbb[1], st.zl[0], s2);
         const float P = wv[p] - fmaf(st.lbb[0], y, s2);
-        const float qz = fminf(fmaxf(rintf(P * st.rc.y) + st.rc.z, st.qminf), st.qmaxf);
-        const float v = st.rc.x * (qz - st.rc.z);
+        // code = clamp(rint(P / s) + z), value s (code - z)
+        float qz, res;
+        if (ZP) {
+            qz = __builtin_amdgcn_fmed3f(rintf(P * st.rc.y) + st.rc.z, st.qminf, st.qmaxf);
+            res = fmaf(-st.rc.x, qz - st.rc.z, P);
+        } else {
+            qz = __builtin_amdgcn_fmed3f(rintf(P * st.rc.y), st.qminf, st.qmaxf);
+            res = fmaf(-st.rc.x, qz, P);
+        }
         const bool act = (unsigned)(d - r) < (unsigned)TB;
-        float e = (P - v) * (st.rc.w * cb.ila[p]);
+        float e = res * (st.rc.w * cb.ila[p]);
         float z = fmaf(e, la[0], y);
+        code[p] = qz;
         *(act ? lf_E + st.e_off + d : lf_sink + r) = e;
         *(act ? lf_Z + st.z_off + d * LP : lf_sink + TB + r) = z;
-        *(act ? lf_C + st.c_off + d : lf_C + TB * TB + r) = (int8_t)(int)qz;
         e = act ? e : 0.0f;
         z = act ? z : 0.0f;
 #pragma unroll
@@ -304,9 +313,13 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
         st.eh[0] = e;
         st.zl[0] = from_lane_above(z);
     }
+    // the block's W slots were read before the block started
+    *reinterpret_cast<float4 *>(st.wrow + LJ * t) = make_float4(code[0], code[1], code[2], code[3]);
 }
 
+template <bool ZP>
 __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const float qmaxf) {
+    __builtin_assume(r >= 0 && r < TB);
     ChainState st;
     st.r = r;
     st.lbb[0] = lf_B[r * LP + r];
@@ -319,19 +332,44 @@ __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const
     for (int j = 0; j < LWIN; ++j) st.eh[j] = st.zl[j] = 0.0f;
     st.e_off = r * (LP - 1);   // E[r][d - r]
     st.z_off = -r * (LP - 1);  // Z^T[d - r][r] at z_off + d LP
-    st.c_off = r * (TB - 1);   // C[r][d - r]
-    const float *wrow = lf_Wk + r * WSP;
+    st.wrow = lf_Wk + r * WSP;
     const float4 *ab = lf_Ab + 2 * (CX - r);  // step d: ab[2d], ab[2d + 1]
     const float *ib = lf_ila + (CX - r);      // step d: ib[d]
     ChainBlock c0, c1;
-    chain_load(c0, wrow, ab, ib, 0);
+    chain_load(c0, st.wrow, ab, ib, 0);
     for (int t = 0; t < NBLK; t += 2) {
-        chain_load(c1, wrow, ab, ib, t + 1);
-        chain_block(st, c0, t);
+        chain_load(c1, st.wrow, ab, ib, t + 1);
+        chain_block<ZP>(st, c0, t);
         __syncthreads();
-        chain_load(c0, wrow, ab, ib, t + 2);
-        chain_block(st, c1, t + 1);
+        chain_load(c0, st.wrow, ab, ib, t + 2);
+        chain_block<ZP>(st, c1, t + 1);
         __syncthreads();
+    }
+}
+
+// The LJ bulk dots of one helper unit over NCH 16-wide chunks of k: every
+// load is issued before the first product.  Elements at or beyond len are
+// masked (the chain may be writing them).
+template <int NCH>
+__device__ __forceinline__ void unit_dots(const float *X, const float *const (&Y)[LJ], int len,
+                                          int q, float (&acc)[LJ]) {
+    float4 x[NCH], y[NCH][LJ];
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        x[ch] = *reinterpret_cast<const float4 *>(X + 16 * ch);
+#pragma unroll
+        for (int p = 0; p < LJ; ++p) y[ch][p] = *reinterpret_cast<const float4 *>(Y[p] + 16 * ch);
+    }
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int k0 = 16 * ch + 4 * q;
+        float4 xm = x[ch];
+        xm.x = k0 < len ? xm.x : 0.0f;
+        xm.y = k0 + 1 < len ? xm.y : 0.0f;
+        xm.z = k0 + 2 < len ? xm.z : 0.0f;
+        xm.w = k0 + 3 < len ? xm.w : 0.0f;
+#pragma unroll
+        for (int p = 0; p < LJ; ++p) acc[p] = dot4(xm, y[ch][p], acc[p]);
     }
 }
 
@@ -339,7 +377,9 @@ __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const
 // (dir 0, row direction, X = E[idx][.], Y = LA rows of the entries' columns) or
 // one column (dir 1, column direction, X = Z[.][idx], Y = LB rows of the
 // entries' rows) over k < len; lane q then holds entry q's total and writes it.
-__device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float *buf, int q) {
+// nch (at least ceil(len / 16)) is uniform over the wave.
+__device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float *buf, int q,
+                                            int nch) {
     const int idx = lo + (u >> 1), dir = u & 1;
     const int len = s0 - idx;
     const float *X = (dir ? lf_Z : lf_E) + idx * LP + 4 * q;
@@ -351,37 +391,12 @@ __device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float
         Y[p] = Yb + clamp_col(D0 + p - idx) * LP;
         acc[p] = 0.0f;
     }
-    const int nfull = len > 0 ? len >> 4 : 0;
-    if (nfull > 0) {
-        float4 x = *reinterpret_cast<const float4 *>(X);
-        float4 y[LJ];
-#pragma unroll
-        for (int p = 0; p < LJ; ++p) y[p] = *reinterpret_cast<const float4 *>(Y[p]);
-        for (int ch = 1; ch < nfull; ++ch) {
-            const float4 xn = *reinterpret_cast<const float4 *>(X + 16 * ch);
-            float4 yn[LJ];
-#pragma unroll
-            for (int p = 0; p < LJ; ++p) yn[p] = *reinterpret_cast<const float4 *>(Y[p] + 16 * ch);
-#pragma unroll
-            for (int p = 0; p < LJ; ++p) acc[p] = dot4(x, y[p], acc[p]);
-            x = xn;
-#pragma unroll
-            for (int p = 0; p < LJ; ++p) y[p] = yn[p];
-        }
-#pragma unroll
-        for (int p = 0; p < LJ; ++p) acc[p] = dot4(x, y[p], acc[p]);
-    }
-    if (len > 0 && (len & 15) != 0) {
-        // tail chunk: elements at or beyond len may be in flux; mask them
-        const int k0 = 16 * nfull + 4 * q;
-        float4 x = *reinterpret_cast<const float4 *>(X + 16 * nfull);
-        x.x = k0 < len ? x.x : 0.0f;
-        x.y = k0 + 1 < len ? x.y : 0.0f;
-        x.z = k0 + 2 < len ? x.z : 0.0f;
-        x.w = k0 + 3 < len ? x.w : 0.0f;
-#pragma unroll
-        for (int p = 0; p < LJ; ++p)
-            acc[p] = dot4(x, *reinterpret_cast<const float4 *>(Y[p] + 16 * nfull), acc[p]);
+    switch (nch) {
+        case 1: unit_dots<1>(X, Y, len, q, acc); break;
+        case 2: unit_dots<2>(X, Y, len, q, acc); break;
+        case 3: unit_dots<3>(X, Y, len, q, acc); break;
+        case 4: unit_dots<4>(X, Y, len, q, acc); break;
+        default: break;
     }
     // 4 x 4 transpose-reduce over the group: lane q ends with entry q's sum
     const bool o1 = q & 1, o2 = q & 2;
@@ -408,20 +423,25 @@ __device__ __forceinline__ void leaf_helpers(const int hl) {
             const int lo = max(0, D0 - (TB - 1)), hi = min(TB - 1, D0 + LJ - 1);
             const int nunit = 2 * (hi - lo + 1);
             float *buf = lf_bulk + ((t + 1) & 1) * 2 * TB * LJ;
-            // units in order of decreasing length, dealt out in a snake
-            static_assert(2 * NG >= 2 * TB, "two unit slots per group cover every unit");
-            if (g < nunit) helper_unit(g, lo, D0, s0, buf, q);
-            if (2 * NG - 1 - g < nunit) helper_unit(2 * NG - 1 - g, lo, D0, s0, buf, q);
+            // one unit per group, units in order of decreasing length: lane 0
+            // of the wave holds its longest unit, whose chunk count every
+            // group of the wave uses (consecutive units differ by one in length)
+            static_assert(NG >= 2 * TB, "one unit slot per group covers every unit");
+            const int g0 = __builtin_amdgcn_readfirstlane(g);
+            const int len0 = s0 - (lo + (g0 >> 1));
+            const int nch = len0 > 0 ? (len0 + 15) >> 4 : 0;
+            if (g < nunit) helper_unit(g, lo, D0, s0, buf, q, nch);
         }
         __syncthreads();
     }
 }
 
-// the wave that shares the chain's SIMD: barriers only
+// the waves that share the chain's SIMD: barriers only
 __device__ __forceinline__ void leaf_idle() {
     for (int t = 0; t < NBLK; ++t) __syncthreads();
 }
 
+template <bool ZP>
 __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K) {
     const int tid = threadIdx.x;
     const int Ilo = max(0, K - a.N + 1);
@@ -461,11 +481,10 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K) {
     __syncthreads();
 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (w == 0) leaf_chain(tid, (float)a.qmin, (float)a.qmax);
-    else if (w == 4) leaf_idle();
-    else leaf_helpers(tid - (w < 4 ? 64 : 128));
+    if (w == 0) leaf_chain<ZP>(tid, (float)a.qmin, (float)a.qmax);
+    else if ((w & 3) == 0) leaf_idle();
+    else leaf_helpers((w - 1 - (w >> 2)) * 64 + (tid & 63));
     const float *Es = lf_E;
-    const int8_t *Cs = lf_C;
     const float4 *s_row = lf_row;
 
     // E tile to the band-update buffer
@@ -490,10 +509,11 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K) {
         const int64_t gi = r0 + r, gj = c0 + c;
         bad |= !isfinite(Es[r * LP + c]);
         if (gi < a.m && gj < a.n) {
-            const int8_t code = Cs[r * TB + c];
+            const float qf = lf_Wk[r * WSP + r + c];
+            const int8_t code = (int8_t)(int)qf;
             a.codes[gi * a.n + gj] = code;
             const float4 rc = s_row[r];
-            if (a.V) a.V[gi * a.n + gj] = rc.x * ((float)code - rc.z);
+            if (a.V) a.V[gi * a.n + gj] = rc.x * (qf - rc.z);
             if (a.E) a.E[gi * a.n + gj] = Es[r * LP + c];
         }
     }
@@ -935,7 +955,10 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_
     for (const Node &nd : nodes) {
         if (nd.leaf) {
             const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
-            hipLaunchKernelGGL(leaf_kernel, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream, la, nd.K);
+            if (sv.qkind == BAKRON_Q_ASYM)
+                hipLaunchKernelGGL(leaf_kernel<true>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream, la, nd.K);
+            else
+                hipLaunchKernelGGL(leaf_kernel<false>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream, la, nd.K);
             BK_LAUNCH_CHECK("leaf_kernel");
             BK_MARK(1);
         } else {
