@@ -141,7 +141,10 @@ def main():
     sched = bakron.schedule_info(m, n, args.order)
     band_launches = sched["band_launches"]
     gemm_avg_s = ph["band_ms"] / 1e3 / band_launches
-    gemm_alg_per_launch = sched["alg_band_flops"] / band_launches
+    # algorithmic flops of the band-GEMM launches: the useful multiply-adds of
+    # their tiles (the zero halves of triangular diagonal factor blocks left
+    # out); the two-diagonal nodes run inside the leaves and are not counted
+    gemm_alg_per_launch = sched["useful_band_flops"] / band_launches
     gemm_tflops = gemm_alg_per_launch / gemm_avg_s / 1e12
     leaf_avg_s = ph["leaf_ms"] / 1e3 / sched["leaf_launches"]
     # leaf algorithmic HBM bytes per entry: W tile in (4), E out (4), codes (1),

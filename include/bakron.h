@@ -137,16 +137,22 @@ int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
 
 /*
  * bakron_schedule_info -- the static schedule for an m x n solve, without
- * touching the GPU.  out[0..9]:
+ * touching the GPU.  out[0..12]:
  *   0 tile size b           1 leaf launches (tile anti-diagonals M+N-1)
  *   2 band GEMM launches    3 sequential in-kernel diagonal steps ((M+N-1)(2b-1))
  *   4 order used (1 = LA first, 2 = LB first)
  *   5 algorithmic band flops: two products per recursion node at single
  *     anti-diagonal granularity (the exact staircase count of Algorithm 6)
- *   6 executed band flops with dense b x b tiles (order of out[4])
+ *   6 flops the band GEMM launches execute with dense b x b tiles (order of out[4])
  *   7 the paper's count F = m n (m + n)
  *   8 in-tile leaf flops executed (two length-b dot products per entry)
  *   9 recursion depth (levels)
+ *  10 useful flops of the band GEMM launches: out[6] without the zero half of
+ *     the triangular diagonal factor blocks
+ *  11 flops of the leaf pulls: a recursion node over two tile diagonals has no
+ *     launch of its own; the leaf of its second diagonal applies its update
+ *     (up to four dense b x b x b products per tile)
+ *  12 leaf launches that pull
  * Returns BAKRON_OK or BAKRON_ERR_INVALID_ARG.
  */
 int32_t bakron_schedule_info(int64_t m, int64_t n, int32_t flags, double *out);

@@ -125,19 +125,48 @@ def test_algorithmic_flops_match_enumeration(lib, m, n):
     assert bakron.schedule_info(m, n)["alg_band_flops"] == _brute_alg_flops(m, n)
 
 
+def _tile_recursion(D):
+    """Band nodes (K, L, H) with a launch of their own (L >= 3) and the leaves
+    that pull a two-diagonal node's update, of the recursion over D tile
+    anti-diagonals (split at floor(L / 2))."""
+    band, pulls = [], []
+
+    def rec(K, L):
+        if L == 1:
+            return
+        if L == 2:
+            pulls.append(K + 1)
+            return
+        H = L // 2
+        rec(K, H)
+        band.append((K, L, H))
+        rec(K + H, L - H)
+
+    rec(0, D)
+    return band, pulls
+
+
 def test_schedule_shape(lib):
     # 4096 x 4096 in 64-tiles: 127 tile anti-diagonals, each swept in 127 steps;
     # O(m + n) sequential steps; product-order choice per shape.
     s = bakron.schedule_info(4096, 4096)
+    band, pulls = _tile_recursion(127)
     assert s["leaf_launches"] == 127 and s["leaf_steps"] == 127 * 127
-    assert s["band_launches"] == 2 * 126
+    assert len(band) + len(pulls) == 126          # every node of the recursion
+    assert s["band_launches"] == 2 * len(band)
+    assert s["pull_leaves"] == len(pulls)
+    tiles = lambda K: [(I, K - I) for I in range(max(0, K - 63), min(63, K) + 1)]
+    prods = sum((2 if I >= 1 else 0) + (2 if J >= 1 else 0) for K in pulls for I, J in tiles(K))
+    assert s["pull_flops"] == prods * 2 * 64 ** 3
     assert s["F"] == 4096 * 4096 * 8192
     assert abs(s["alg_band_flops"] / 2.369e11 - 1) < 1e-3
-    # executed dense-tile flops never fall below the algorithmic count
+    # the band launches and the leaf pulls together never execute fewer flops
+    # than the algorithmic count; the useful part excludes triangle zeros only
     for (m, n) in [(1024, 1024), (11008, 4096), (4096, 14336)]:
         for order in (1, 2):
             si = bakron.schedule_info(m, n, order)
-            assert si["exec_band_flops"] >= si["alg_band_flops"] * 0.999
+            assert si["exec_band_flops"] + si["pull_flops"] >= si["alg_band_flops"] * 0.999
+            assert 0.9 * si["exec_band_flops"] < si["useful_band_flops"] <= si["exec_band_flops"]
     assert bakron.schedule_info(11008, 4096)["order"] == 1
     assert bakron.schedule_info(4096, 14336)["order"] == 2
     # a single tile has no band update

@@ -157,12 +157,13 @@ def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_
 
 
 SCHEDULE_KEYS = ("tile", "leaf_launches", "band_launches", "leaf_steps", "order",
-                 "alg_band_flops", "exec_band_flops", "F", "leaf_flops", "depth")
+                 "alg_band_flops", "exec_band_flops", "F", "leaf_flops", "depth",
+                 "useful_band_flops", "pull_flops", "pull_leaves")
 
 
 def schedule_info(m: int, n: int, order: int = ORDER_AUTO) -> dict:
     lib = load()
-    buf = (ctypes.c_double * 10)()
+    buf = (ctypes.c_double * len(SCHEDULE_KEYS))()
     _check(lib.bakron_schedule_info(m, n, order, buf), "bakron_schedule_info")
     return dict(zip(SCHEDULE_KEYS, list(buf)))
 

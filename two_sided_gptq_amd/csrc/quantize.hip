@@ -150,6 +150,7 @@ struct LeafArgs {
     float *V, *E;
     int64_t m, n;
     int32_t *dev_status;
+    float *Cd, *Cr;   // contributions of the previous tile diagonal: from the tile above / to the left
 };
 
 // sum over the 4 consecutive lanes of a group (all 4 end with the total)
@@ -222,6 +223,7 @@ __shared__ float lf_ila[NCX];                    // CX + c: 1 / LA_cc; 0 off 0..
 __shared__ float4 lf_row[TB];                    // (s, 1/s, z, 1/LB_rr)
 __shared__ __align__(16) float lf_bulk[2 * 2 * TB * LJ];  // [buffer][direction][row][step in block]
 __shared__ float lf_sink[3 * TB];                // write targets of idle lanes
+__shared__ __align__(16) float lf_P[2 * TB * GP]; // push operands: LA(J+1,J), then LB(I+1,I)
 
 // the value lane l-1 holds, in lane l (lane 0 gets 0): a whole-wave shift
 __device__ __forceinline__ float from_lane_above(float x) {
@@ -436,22 +438,121 @@ __device__ __forceinline__ void leaf_helpers(const int hl) {
     }
 }
 
+// ------------------------------------------------------------ leaf push
+// A recursion node over two tile diagonals [K, K+2) has a band update from
+// diagonal K to K+1 alone.  It gets no launch: the leaf of diagonal K, which
+// holds E(I,J), LA(J,J) and LB(I,I) in LDS and has prefetched LA(J+1,J) and
+// LB(I+1,I), computes the two contributions of its tile,
+//   to (I+1, J):  LB(I+1,I) (E(I,J) LA(J,J)^T)
+//   to (I, J+1):  LB(I,I) (E(I,J) LA(J+1,J)^T),
+// into the workspace, and the leaf of diagonal K+1 subtracts them while it
+// loads its W tile.  fp32 MFMA on 32 x 32 quadrants (waves 0-3, one per
+// SIMD); lane l supplies row l % 32 of both operands and the k half l / 32; the
+// triangular diagonal blocks cut the k range of the quadrants that allow it.
+
+// acc += A[i][k] B[j][k]^T over k < KN for the 32 x 32 block; fa(i, k), fb(j, k)
+// return the float4 at k .. k+3 of row i (j) of the block.
+template <int KN, class FA, class FB>
+__device__ __forceinline__ void mfma_block(floatx16 &acc, FA fa, FB fb) {
+    const int lane = threadIdx.x & 63, i = lane & 31, k0 = (lane >> 5) * (KN / 2);
+#pragma unroll
+    for (int s4 = 0; s4 < KN / 8; ++s4) {
+        const float4 av = fa(i, k0 + 4 * s4);
+        const float4 bv = fb(i, k0 + 4 * s4);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ float4 lds4(const float *base, int stride, int row, int k) {
+    return *reinterpret_cast<const float4 *>(base + row * stride + k);
+}
+
+// waves 0-3: quadrant (w >> 1, w & 1).  Phase 1 stores U^T and V^T (stride
+// GP) in lf_Z and in the skewed-W area, both free once the sweep's outputs are
+// written; phase 2 writes the contributions.
+__device__ __forceinline__ void leaf_push(const LeafArgs &a, int I, int J, int w, bool phase2) {
+    const int lane = threadIdx.x & 63;
+    const int qr = w >> 1, qc = w & 1;
+    const bool down = I + 1 < a.M, right = J + 1 < a.N;
+    const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
+    const int rb = 32 * qr, cb = 32 * qc;
+    float *Ut = lf_Z, *Vt = lf_Wk;
+    floatx16 acc, acc2;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = acc2[v] = 0.0f;
+    if (!phase2) {
+        if (down) {  // U = E LA(J,J)^T
+            auto fa = [&](int i, int k) { return lds4(lf_E, LP, rb + i, k); };
+            auto fb = [&](int j, int k) { return lds4(lf_A, LP, cb + j, k); };
+            if (qc) mfma_block<64>(acc, fa, fb);
+            else mfma_block<32>(acc, fa, fb);
+        }
+        if (right) {  // V = E LA(J+1,J)^T
+            auto fa = [&](int i, int k) { return lds4(lf_E, LP, rb + i, k); };
+            auto fb = [&](int j, int k) { return lds4(lf_P, GP, cb + j, k); };
+            mfma_block<64>(acc2, fa, fb);
+        }
+        // accumulator: lane holds column lane % 32, register v row 8(v/4) + 4(lane/32) + v%4
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int rr = rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cc = cb + (lane & 31);
+            Ut[cc * GP + rr] = acc[v];
+            Vt[cc * GP + rr] = acc2[v];
+        }
+    } else {
+        if (down) {  // LB(I+1,I) U
+            auto fa = [&](int i, int k) { return lds4(lf_P + TB * GP, GP, rb + i, k); };
+            auto fb = [&](int j, int k) { return lds4(Ut, GP, cb + j, k); };
+            mfma_block<64>(acc, fa, fb);
+        }
+        if (right) {  // LB(I,I) V
+            auto fa = [&](int i, int k) { return lds4(lf_B, LP, rb + i, k); };
+            auto fb = [&](int j, int k) { return lds4(Vt, GP, cb + j, k); };
+            if (qr) mfma_block<64>(acc2, fa, fb);
+            else mfma_block<32>(acc2, fa, fb);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t rr = rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cc = cb + (lane & 31);
+            if (down) a.Cd[(r0 + TB + rr) * a.np + c0 + cc] = acc[v];
+            if (right) a.Cr[(r0 + rr) * a.np + c0 + TB + cc] = acc2[v];
+        }
+    }
+}
+
 // the waves that share the chain's SIMD: barriers only
 __device__ __forceinline__ void leaf_idle() {
     for (int t = 0; t < NBLK; ++t) __syncthreads();
 }
 
+// flags: LEAF_PULL subtract the contributions pushed by the previous leaf;
+// LEAF_PUSH compute this tile's contributions to the next tile diagonal
+constexpr int LEAF_PULL = 1, LEAF_PUSH = 2;
+
 template <bool ZP>
-__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K) {
+__global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, int flags) {
     const int tid = threadIdx.x;
     const int Ilo = max(0, K - a.N + 1);
     const int I = Ilo + blockIdx.x;
     const int J = K - I;
     const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
 
+    const bool pull_up = (flags & LEAF_PULL) && I >= 1, pull_left = (flags & LEAF_PULL) && J >= 1;
     for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
         const int r = idx >> 4, c4 = (idx & 15) * 4;
-        const float4 wv = *reinterpret_cast<const float4 *>(a.Wp + (r0 + r) * a.np + c0 + c4);
+        const int64_t g = (r0 + r) * a.np + c0 + c4;
+        float4 wv = *reinterpret_cast<const float4 *>(a.Wp + g);
+        if (pull_up) {
+            const float4 d = *reinterpret_cast<const float4 *>(a.Cd + g);
+            wv.x -= d.x; wv.y -= d.y; wv.z -= d.z; wv.w -= d.w;
+        }
+        if (pull_left) {
+            const float4 d = *reinterpret_cast<const float4 *>(a.Cr + g);
+            wv.x -= d.x; wv.y -= d.y; wv.z -= d.z; wv.w -= d.w;
+        }
         float *wk = lf_Wk + r * WSP + r + c4;
         wk[0] = wv.x;
         wk[1] = wv.y;
@@ -461,6 +562,17 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K) {
             *reinterpret_cast<const float4 *>(a.LBp + (r0 + r) * a.mp + r0 + c4);
         *reinterpret_cast<float4 *>(lf_A + r * LP + c4) =
             *reinterpret_cast<const float4 *>(a.LAp + (c0 + r) * a.np + c0 + c4);
+    }
+    if (flags & LEAF_PUSH) {
+        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
+            const int r = idx >> 4, c4 = (idx & 15) * 4;
+            if (J + 1 < a.N)
+                *reinterpret_cast<float4 *>(lf_P + r * GP + c4) =
+                    *reinterpret_cast<const float4 *>(a.LAp + (c0 + TB + r) * a.np + c0 + c4);
+            if (I + 1 < a.M)
+                *reinterpret_cast<float4 *>(lf_P + (TB + r) * GP + c4) =
+                    *reinterpret_cast<const float4 *>(a.LBp + (r0 + TB + r) * a.mp + r0 + c4);
+        }
     }
     for (int idx = tid; idx < 2 * 2 * TB * LJ / 4; idx += LEAF_THREADS)
         reinterpret_cast<float4 *>(lf_bulk)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -518,6 +630,12 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K) {
         }
     }
     if (bad && a.dev_status) atomicOr(a.dev_status, BAKRON_DEV_NONFINITE);
+    if (flags & LEAF_PUSH) {
+        __syncthreads();  // the skewed-W area (codes) has been read
+        if (w < 4) leaf_push(a, I, J, w, false);
+        __syncthreads();
+        if (w < 4) leaf_push(a, I, J, w, true);
+    }
 }
 
 // -------------------------------------------------------------- band GEMMs
@@ -568,8 +686,12 @@ __device__ inline bool band_tile(const BandArgs &g, int bx, int by, int &ci, int
 // contiguous float4 from LDS.  The next K block is prefetched into registers
 // while the current one is multiplied.
 __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
+    // longest tiles first: the K depth grows with the band offset in every
+    // mode and with the row in the second products, so those run backwards
+    const int bx = gridDim.x - 1 - blockIdx.x;
+    const int by = (g.mode == 1 || g.mode == 3) ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
     int ci, cj, klo, khi;
-    if (!band_tile(g, blockIdx.x, blockIdx.y, ci, cj, klo, khi)) return;
+    if (!band_tile(g, bx, by, ci, cj, klo, khi)) return;
     __shared__ __align__(16) float As[TB * GP];
     __shared__ __align__(16) float Bs[TB * GP];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -678,17 +800,23 @@ __global__ __launch_bounds__(256) void sumsq_final_kernel(const double *partial,
 // ---------------------------------------------------------------- schedule
 struct Node {
     int leaf;  // 1: leaf(K); 0: band(K, L, H)
+    int flags;  // leaf only: LEAF_PUSH / LEAF_PULL (two-diagonal nodes run inside the leaves)
     int K, L, H;
 };
 
 void build_nodes(int K, int L, std::vector<Node> &out) {
     if (L == 1) {
-        out.push_back({1, K, 1, 0});
+        out.push_back({1, 0, K, 1, 0});
+        return;
+    }
+    if (L == 2) {  // leaf(K), band(K, 2, 1), leaf(K+1): the band runs inside the two leaves
+        out.push_back({1, LEAF_PUSH, K, 1, 0});
+        out.push_back({1, LEAF_PULL, K + 1, 1, 0});
         return;
     }
     const int H = L / 2;  // split of the range [K, K+L) at K + floor(L/2)
     build_nodes(K, H, out);
-    out.push_back({0, K, L, H});
+    out.push_back({0, 0, K, L, H});
     build_nodes(K + H, L - H, out);
 }
 
@@ -725,39 +853,71 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
     p2.cols = L - H;
 }
 
-// executed band flops with dense tiles for one order (host mirror of band_tile)
-double executed_band_flops(int order, int M, int N) {
+// Flops of the band-GEMM launches of one order (host mirror of band_tile):
+// exec counts every dense 64 x 64 x 64 tile step; useful leaves out the zero
+// half of a triangular diagonal factor block (LA(J,J) or LB(I,I)).
+struct BandCount {
+    double exec, useful;
+    int launches;
+};
+
+BandCount band_flops(int order, int M, int N) {
     std::vector<Node> nodes;
     build_nodes(0, M + N - 1, nodes);
-    double macs_tiles = 0;
+    double full = 0, diag = 0;
+    int launches = 0;
     for (const Node &nd : nodes) {
         if (nd.leaf) continue;
         Launch p[2];
         band_launches(order, nd.K, nd.L, nd.H, M, N, p[0], p[1]);
         for (int s = 0; s < 2; ++s) {
+            if (p[s].rows <= 0) continue;
+            ++launches;
             for (int y = 0; y < p[s].rows; ++y)
                 for (int x = 0; x < p[s].cols; ++x) {
                     const int K = nd.K, H = nd.H, row = p[s].rlo + y, o = x;
-                    int lo, hi;
+                    int lo, hi, fac;  // fac: k block holding the factor's diagonal block
                     if (p[s].mode == 0) {
                         const int Jp = K - row + o;
                         if (Jp < 0 || Jp >= N) continue;
-                        lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1 - row);
+                        lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1 - row); fac = Jp;
                     } else if (p[s].mode == 2) {
                         const int Ip = K - row + o;
                         if (Ip < 0 || Ip >= M) continue;
-                        lo = std::max(0, K - row); hi = std::min(Ip, K + H - 1 - row);
+                        lo = std::max(0, K - row); hi = std::min(Ip, K + H - 1 - row); fac = Ip;
                     } else {
                         const int Jp = K + H + o - row;
                         if (Jp < 0 || Jp >= N) continue;
-                        if (p[s].mode == 1) { lo = std::max(0, K - Jp); hi = std::min(row, K + H - 1); }
-                        else { lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1); }
+                        if (p[s].mode == 1) { lo = std::max(0, K - Jp); hi = std::min(row, K + H - 1); fac = row; }
+                        else { lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1); fac = Jp; }
                     }
-                    if (hi >= lo) macs_tiles += hi - lo + 1;
+                    if (hi < lo) continue;
+                    full += hi - lo + 1;
+                    if (fac >= lo && fac <= hi) diag += 1;
                 }
         }
     }
-    return macs_tiles * 2.0 * TB * TB * TB;
+    const double tile = 2.0 * TB * TB * TB;
+    return BandCount{full * tile, (full - diag) * tile + diag * (2.0 * TB * TB * (TB + 1) / 2), launches};
+}
+
+// Two-diagonal nodes: every leaf that pushes runs up to two products per
+// target tile (dense 64 x 64 x 64 fp32 MFMA).
+void pull_counts(int M, int N, double *flops, int *leaves) {
+    std::vector<Node> nodes;
+    build_nodes(0, M + N - 1, nodes);
+    double f = 0;
+    int nl = 0;
+    for (const Node &nd : nodes) {
+        if (!nd.leaf || !(nd.flags & LEAF_PUSH)) continue;
+        ++nl;
+        for (int I = std::max(0, nd.K - N + 1); I <= std::min(M - 1, nd.K); ++I) {
+            const int J = nd.K - I;
+            f += (I + 1 < M ? 2 : 0) + (J + 1 < N ? 2 : 0);
+        }
+    }
+    *flops = f * 2.0 * TB * TB * TB;
+    *leaves = nl;
 }
 
 // Algorithm 6 at single anti-diagonal granularity (product order LA first):
@@ -803,7 +963,9 @@ double algorithmic_band_flops(int64_t m, int64_t n) {
 }
 
 struct ShapeInfo {
-    double exec_flops[3];  // index by order (1, 2)
+    BandCount band[3];  // index by order (1, 2)
+    double pull_flops;
+    int pull_leaves;
     int auto_order;
 };
 
@@ -816,9 +978,10 @@ const ShapeInfo &shape_info(int M, int N) {
     auto it = g_shapes.find(key);
     if (it != g_shapes.end()) return it->second;
     ShapeInfo s{};
-    s.exec_flops[1] = executed_band_flops(BAKRON_ORDER_LA_FIRST, M, N);
-    s.exec_flops[2] = executed_band_flops(BAKRON_ORDER_LB_FIRST, M, N);
-    s.auto_order = s.exec_flops[2] < s.exec_flops[1] ? BAKRON_ORDER_LB_FIRST : BAKRON_ORDER_LA_FIRST;
+    s.band[1] = band_flops(BAKRON_ORDER_LA_FIRST, M, N);
+    s.band[2] = band_flops(BAKRON_ORDER_LB_FIRST, M, N);
+    pull_counts(M, N, &s.pull_flops, &s.pull_leaves);
+    s.auto_order = s.band[2].exec < s.band[1].exec ? BAKRON_ORDER_LB_FIRST : BAKRON_ORDER_LA_FIRST;
     return g_shapes.emplace(key, s).first->second;
 }
 
@@ -826,7 +989,7 @@ thread_local bool g_phase_valid = false;
 thread_local double g_phase_ms[6];
 
 struct Buffers {
-    float *Wp, *Ebuf, *Tbuf, *LAp, *LBp, *sc, *zp;
+    float *Wp, *Ebuf, *Tbuf, *LAp, *LBp, *sc, *zp, *Cd, *Cr;
     double *partial;
 };
 
@@ -840,7 +1003,9 @@ size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     float *sc = cv.take<float>(mp);
     float *zp = cv.take<float>(mp);
     double *part = cv.take<double>(NPART);
-    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, part};
+    float *Cd = cv.take<float>(mp * np);
+    float *Cr = cv.take<float>(mp * np);
+    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part};
     return cv.used;
 }
 
@@ -875,14 +1040,17 @@ extern "C" int32_t bakron_schedule_info(int64_t m, int64_t n, int32_t flags, dou
     const int D = M + N - 1;
     out[0] = TB;
     out[1] = D;
-    out[2] = 2.0 * (D - 1);
+    out[2] = si.band[order].launches;
     out[3] = (double)D * (2 * TB - 1);
     out[4] = order;
     out[5] = algorithmic_band_flops(m, n);
-    out[6] = si.exec_flops[order];
+    out[6] = si.band[order].exec;
     out[7] = (double)m * (double)n * (double)(m + n);
     out[8] = (double)M * N * TB * TB * 4.0 * TB;
     out[9] = depth_of(D);
+    out[10] = si.band[order].useful;
+    out[11] = si.pull_flops;
+    out[12] = si.pull_leaves;
     return BAKRON_OK;
 }
 
@@ -948,7 +1116,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_
     BK_MARK(0);
 
     LeafArgs la{b.Wp, b.Ebuf, b.LAp, b.LBp, b.sc, b.zp, mp, np, M, N, sv.order, sv.qmin, sv.qmax,
-                sv.codes, sv.V, sv.E, m, n, sv.dev_status};
+                sv.codes, sv.V, sv.E, m, n, sv.dev_status, b.Cd, b.Cr};
     std::vector<Node> nodes;
     nodes.reserve(2 * (M + N));
     build_nodes(0, M + N - 1, nodes);
@@ -956,9 +1124,11 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_
         if (nd.leaf) {
             const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
             if (sv.qkind == BAKRON_Q_ASYM)
-                hipLaunchKernelGGL(leaf_kernel<true>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream, la, nd.K);
+                hipLaunchKernelGGL(leaf_kernel<true>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream,
+                                   la, nd.K, nd.flags);
             else
-                hipLaunchKernelGGL(leaf_kernel<false>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream, la, nd.K);
+                hipLaunchKernelGGL(leaf_kernel<false>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream,
+                                   la, nd.K, nd.flags);
             BK_LAUNCH_CHECK("leaf_kernel");
             BK_MARK(1);
         } else {
