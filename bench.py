@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 FP32_MFMA_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
+PROFILE_MD = os.path.join(ROOT, "profiles", "band_gemm_leaf_4096x4096_int4.md")
 
 
 def parse():
@@ -152,9 +153,13 @@ def main():
     leaf_bytes = m * n * (4 + 4 + 1 + 4 + 8.0 / 64)
     leaf_gbs = leaf_bytes / sched["leaf_launches"] / leaf_avg_s / 1e9
     dominant = "band_gemm" if ph["band_ms"] >= ph["leaf_ms"] else "leaf"
+    # HBM bytes per band-GEMM dispatch from the committed rocprofv3 counter
+    # summary, null unless it was taken from the current kernel source
+    from two_sided_gptq_amd import profsum
+    traffic = profsum.read_traffic(PROFILE_MD, "band_gemm_kernel")
     roofline = {"kernel": "band_gemm_kernel", "bound": "mfma", "achieved": gemm_tflops,
                 "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": gemm_tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+                "frac": gemm_tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": traffic,
                 "alg_flops_per_launch": gemm_alg_per_launch, "avg_launch_ms": gemm_avg_s * 1e3,
                 "launches": band_launches}
 

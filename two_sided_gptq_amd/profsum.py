@@ -1,0 +1,132 @@
+"""Summarise rocprofv3 output of the benchmark into a short markdown profile.
+
+    python -m two_sided_gptq_amd.profsum --trace DIR --pmc DIR --out profiles/X.md
+
+DIR of --trace holds `bench_kernel_trace.csv` and `bench_kernel_stats.csv`
+(`rocprofv3 --kernel-trace --stats --output-format csv -o bench`); DIR of --pmc
+holds `FETCH_SIZE/run_counter_collection.csv` and `WRITE_SIZE/...` (one
+`rocprofv3 --pmc <counter> -o run` pass each, with `bench.py --copy-probe`).
+
+HBM bytes per dispatch: FETCH_SIZE and WRITE_SIZE (KiB) are each scaled so that
+the 1 GiB device copy the benchmark runs with --copy-probe reads and writes
+exactly 1 GiB.  The summary records a hash of the kernel source; `bench.py`
+reports the measured traffic only while the source still has that hash.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import os
+import re
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "csrc", "quantize.hip")
+COPY_BYTES = 1 << 30
+
+
+def source_hash(path: str = KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def short_name(n: str) -> str:
+    m = re.match(r"(?:void )?(?:[\w:]*\(anonymous namespace\)::)?([\w:<>, ]+?)\(", n)
+    return m.group(1) if m else n[:48]
+
+
+def _window(rows):
+    """Dispatches of the last timed solve: between the last two parameter kernels."""
+    rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
+    q = [i for i, r in enumerate(rows) if "qparams_kernel" in r["Kernel_Name"]]
+    return rows[q[-2]:q[-1]] if len(q) >= 2 else rows
+
+
+def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> str:
+    out = []
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_trace.csv"))))
+    win = _window(rows)
+    per = collections.defaultdict(list)
+    for r in win:
+        per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    span = int(win[-1]["End_Timestamp"]) - int(win[0]["Start_Timestamp"])
+    out.append(f"Kernel trace command: `{command}`\n")
+    out.append(f"### One solve (last timed bakron_quantize call): {span / 1e3:.1f} us over {len(win)} dispatches\n")
+    out.append("| kernel | launches | total us | avg us | min us | max us |")
+    out.append("|---|---|---|---|---|---|")
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {k} | {len(v)} | {sum(v) / 1e3:.1f} | {statistics.mean(v) / 1e3:.2f} | "
+                   f"{min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
+    out.append("\n### rocprofv3 --stats (whole command)\n")
+    out.append("| kernel | calls | average ns | % |")
+    out.append("|---|---|---|---|")
+    for r in csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_stats.csv"))):
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    # counters
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        for r in csv.DictReader(open(os.path.join(pmc_dir, c, "run_counter_collection.csv"))):
+            vals[short_name(r["Kernel_Name"])][c].append(float(r["Counter_Value"]))
+    copies = vals.get("__amd_rocclr_copyBuffer", {})
+    f_copy = max(copies.get("FETCH_SIZE", [0.0]))
+    w_copy = max(copies.get("WRITE_SIZE", [0.0]))
+    f_scale = COPY_BYTES / (f_copy * 1024) if f_copy else float("nan")
+    w_scale = COPY_BYTES / (w_copy * 1024) if w_copy else float("nan")
+    out.append(f"\n### HBM bytes (counter command: `{pmc_command}`)\n")
+    out.append(f"1 GiB copy probe: FETCH_SIZE {f_copy:.0f} KiB, WRITE_SIZE {w_copy:.0f} KiB "
+               f"-> scale x{f_scale:.3f} (fetch), x{w_scale:.3f} (write).\n")
+    out.append("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes per dispatch (scaled) |")
+    out.append("|---|---|---|---|---|")
+    traffic = {}
+    for k, d in vals.items():
+        if not d.get("FETCH_SIZE") or not d.get("WRITE_SIZE"):
+            continue
+        f = statistics.mean(d["FETCH_SIZE"])
+        w = statistics.mean(d["WRITE_SIZE"])
+        b = (f * f_scale + w * w_scale) * 1024
+        traffic[k] = b
+        out.append(f"| {k} | {len(d['FETCH_SIZE'])} | {f:.1f} | {w:.1f} | {b:.4g} |")
+    out.append("\nMachine-readable (read by bench.py):\n")
+    out.append(f"    source_sha256_16: {source_hash()}")
+    for k in ("band_gemm_kernel", "leaf_kernel<false>"):
+        if k in traffic:
+            out.append(f"    traffic_bytes_per_dispatch: {k} {traffic[k]:.6g}")
+    return "\n".join(out) + "\n"
+
+
+def read_traffic(md_path: str, kernel: str):
+    """Bytes per dispatch of `kernel` from a summary, or None when the summary is
+    missing or was taken from a different kernel source."""
+    try:
+        text = open(md_path).read()
+    except OSError:
+        return None
+    m = re.search(r"source_sha256_16: (\w+)", text)
+    if not m or m.group(1) != source_hash():
+        return None
+    m = re.search(r"traffic_bytes_per_dispatch: " + re.escape(kernel) + r" ([\d.e+]+)", text)
+    return float(m.group(1)) if m else None
+
+
+def main():
+    p = argparse.ArgumentParser()
+    p.add_argument("--trace", required=True)
+    p.add_argument("--pmc", required=True)
+    p.add_argument("--out", required=True)
+    p.add_argument("--command", default="rocprofv3 --kernel-trace --stats --output-format csv "
+                   "-d <trace dir> -o bench -- python3 bench.py --steps 3 --warmup 1 --cpu-sample 0")
+    p.add_argument("--pmc-command", default="rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv "
+                   "-d <pmc dir>/<counter> -o run -- python3 bench.py --steps 1 --warmup 0 "
+                   "--cpu-sample 0 --copy-probe")
+    a = p.parse_args()
+    text = summarise(a.trace, a.pmc, a.command, a.pmc_command)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(a.out)
+
+
+if __name__ == "__main__":
+    main()
