@@ -203,6 +203,7 @@ constexpr int NBLK = (2 * TB - 1 + LJ - 1) / LJ;    // blocks covering the sweep
 constexpr int NSTEP = NBLK * LJ;                    // steps including the idle tail
 constexpr int LEAF_THREADS = 768;                   // 12 waves, three per SIMD
 constexpr int NHELP = 576;                          // helper lanes: every wave not on SIMD 0
+static_assert(NHELP / 64 == 9 && 16 * 8 == 2 * TB, "nine helper waves cover 8 blocks of 16 units");
 // wave 0 is the chain; waves 4 and 8 (on the chain's SIMD) only take part in
 // the barriers, so the chain has its SIMD to itself
 constexpr int WSP = NSTEP + 4;                      // row stride of the skewed W copy
@@ -263,8 +264,13 @@ struct ChainState {
     int r, e_off, z_off;
 };
 
+// Block t: the bulk of its steps is read first (it is the only operand the
+// helpers wrote during the previous block), then the next block's constant
+// operands are requested, then the LJ steps run.
 template <bool ZP>
-__device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb, int t) {
+__device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb, ChainBlock &next,
+                                            const float *wrow, const float4 *ab, const float *ib,
+                                            int t) {
     const int r = st.r;
     float bulk1[LJ], bulk2[LJ], code[LJ];
 #pragma unroll
@@ -272,6 +278,7 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
         bulk1[p] = lf_bulk[(((t & 1) * 2 + 0) * TB + r) * LJ + p];
         bulk2[p] = lf_bulk[(((t & 1) * 2 + 1) * TB + r) * LJ + p];
     }
+    chain_load(next, wrow, ab, ib, t + 1);
     const float wv[4] = {cb.w4.x, cb.w4.y, cb.w4.z, cb.w4.w};
 #pragma unroll
     for (int p = 0; p < LJ; ++p) {
@@ -340,11 +347,9 @@ __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const
     ChainBlock c0, c1;
     chain_load(c0, st.wrow, ab, ib, 0);
     for (int t = 0; t < NBLK; t += 2) {
-        chain_load(c1, st.wrow, ab, ib, t + 1);
-        chain_block<ZP>(st, c0, t);
+        chain_block<ZP>(st, c0, c1, st.wrow, ab, ib, t);
         __syncthreads();
-        chain_load(c0, st.wrow, ab, ib, t + 2);
-        chain_block<ZP>(st, c1, t + 1);
+        chain_block<ZP>(st, c1, c0, st.wrow, ab, ib, t + 1);
         __syncthreads();
     }
 }
@@ -364,12 +369,16 @@ __device__ __forceinline__ void unit_dots(const float *X, const float *const (&Y
     }
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        const int k0 = 16 * ch + 4 * q;
         float4 xm = x[ch];
-        xm.x = k0 < len ? xm.x : 0.0f;
-        xm.y = k0 + 1 < len ? xm.y : 0.0f;
-        xm.z = k0 + 2 < len ? xm.z : 0.0f;
-        xm.w = k0 + 3 < len ? xm.w : 0.0f;
+        // the units of a wave differ by at most 8 in length, so only its last
+        // two chunks can reach beyond a unit's length
+        if (ch + 2 >= NCH) {
+            const int k0 = 16 * ch + 4 * q;
+            xm.x = k0 < len ? xm.x : 0.0f;
+            xm.y = k0 + 1 < len ? xm.y : 0.0f;
+            xm.z = k0 + 2 < len ? xm.z : 0.0f;
+            xm.w = k0 + 3 < len ? xm.w : 0.0f;
+        }
 #pragma unroll
         for (int p = 0; p < LJ; ++p) acc[p] = dot4(xm, y[ch][p], acc[p]);
     }
@@ -414,10 +423,14 @@ __device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float
     *dst = tot;
 }
 
-// helper waves; hl = helper lane 0..NHELP-1, groups of 4 lanes
-__device__ __forceinline__ void leaf_helpers(const int hl) {
-    const int g = hl >> 2, q = hl & 3;
-    constexpr int NG = NHELP / 4;
+// helper waves: hw = 0..8 (SIMD 1 + hw % 3), lane groups of 4.  Units are
+// taken in order of decreasing length, 16 to a wave; the blocks of 16 are
+// dealt to the waves in a snake over the three SIMDs (longest to the first
+// wave of each SIMD, then back), so every SIMD gets a similar share.
+__device__ __forceinline__ void leaf_helpers(const int hw, const int lane) {
+    constexpr int kBlockOf[9] = {0, 1, 2, 5, 4, 3, 6, 7, 8};
+    const int q = lane & 3;
+    const int g = 16 * kBlockOf[hw] + (lane >> 2);  // this group's unit rank
     for (int t = 0; t < NBLK; ++t) {
         if (t + 1 < NBLK) {
             // bulk of block t+1: diagonals D0 .. D0+LJ-1, terms of steps < s0
@@ -425,10 +438,8 @@ __device__ __forceinline__ void leaf_helpers(const int hl) {
             const int lo = max(0, D0 - (TB - 1)), hi = min(TB - 1, D0 + LJ - 1);
             const int nunit = 2 * (hi - lo + 1);
             float *buf = lf_bulk + ((t + 1) & 1) * 2 * TB * LJ;
-            // one unit per group, units in order of decreasing length: lane 0
-            // of the wave holds its longest unit, whose chunk count every
-            // group of the wave uses (consecutive units differ by one in length)
-            static_assert(NG >= 2 * TB, "one unit slot per group covers every unit");
+            // lane 0 of the wave holds its longest unit, whose chunk count every
+            // group of the wave uses
             const int g0 = __builtin_amdgcn_readfirstlane(g);
             const int len0 = s0 - (lo + (g0 >> 1));
             const int nch = len0 > 0 ? (len0 + 15) >> 4 : 0;
@@ -595,7 +606,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (w == 0) leaf_chain<ZP>(tid, (float)a.qmin, (float)a.qmax);
     else if ((w & 3) == 0) leaf_idle();
-    else leaf_helpers((w - 1 - (w >> 2)) * 64 + (tid & 63));
+    else leaf_helpers(w - 1 - (w >> 2), tid & 63);
     const float *Es = lf_E;
     const float4 *s_row = lf_row;
 
