@@ -6,16 +6,31 @@
 // with J the exchange matrix, let G = J H J = C C^T (ordinary lower Cholesky);
 // then H^-1 = J C^-T C^-1 J = (J C^-T J)(J C^-T J)^T and J C^-T J is lower
 // triangular with a positive diagonal, so L = J C^-T J, i.e.
-// L[a][b] = (C^-1)[d-1-b][d-1-a].  One Cholesky and one triangular inverse,
-// both blocked in 64 x 64 tiles and computed in fp64; L is rounded to fp32.
+// L[a][b] = (C^-1)[d-1-b][d-1-a].
+//
+// C and X = C^-1 come from one recursion in fp64 (L is rounded to fp32 at the
+// end).  For a diagonal block split as [G11 .; G21 G22]:
+//   (C11, X11) = recurse(G11)
+//   C21  = G21 X11^T                 (the panel solve, as a product)
+//   G22 -= C21 C21^T                 (lower tiles only)
+//   (C22, X22) = recurse(G22)
+//   X21  = -X22 (C21 X11)
+// down to 64 x 64 blocks, which one workgroup factors and inverts in LDS.  The
+// products run on fp64 MFMA (v_mfma_f64_16x16x4f64) in 64 x 64 output tiles,
+// skipping the k blocks where a triangular operand is zero.
+#include <vector>
+
 #include "common.hpp"
 
 namespace bakron {
 namespace {
 
 constexpr int FT = 64;
-constexpr int FP = 65;  // LDS row stride (doubles) for in-block solves
-constexpr int KC = 16;  // K chunk of the tile products
+constexpr int FP = 65;   // LDS row stride (doubles) of the base block
+constexpr int GK = 16;   // k chunk of the products
+constexpr int GS = GK + 1;
+
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 // G (dp x dp) = J H J on the leading d x d block (lower triangle of H read
 // only), identity on the padding.
@@ -36,181 +51,147 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float *__restr
     }
 }
 
-// unblocked Cholesky of the diagonal block (kb, kb), in place, upper part zeroed
-__global__ __launch_bounds__(256) void chol_diag_kernel(double *G, int64_t dp, int kb,
-                                                        int32_t *dev_status) {
+// One 64 x 64 diagonal block at (off, off): its Cholesky factor and the
+// inverse of that factor, in LDS, right-looking and interleaved.  At column j:
+//   phase 1  c_jj = sqrt(A_jj); column j below the diagonal / c_jj; row j of
+//            X = C^-1 from its completed pending sums: X_jj = 1 / c_jj,
+//            X_jc = -S_jc / c_jj (c < j)
+//   phase 2  trailing update A_ik -= C_ij C_kj (j < k <= i) and pending sums
+//            S_ic += C_ij X_jc (i > j, c <= j)
+// with a barrier after each phase.  Thread (i, q) = (t / 4, t % 4) takes the
+// entries of row i with column = q (mod 4).  Writes the block of C (upper
+// part zero) and of X.
+__global__ __launch_bounds__(256) void base_kernel(const double *__restrict__ G, double *C, double *X,
+                                                   int64_t dp, int64_t off, int32_t *dev_status) {
     __shared__ double A[FT * FP];
+    __shared__ double S[FT * FP];  // pending sums of X, then X
     __shared__ int s_bad;
-    const int t = threadIdx.x;
-    double *blk = G + (int64_t)kb * FT * dp + (int64_t)kb * FT;
-    for (int idx = t; idx < FT * FT; idx += 256) A[(idx / FT) * FP + idx % FT] = blk[(idx / FT) * dp + idx % FT];
+    const int t = threadIdx.x, ri = t >> 2, q = t & 3;
+    for (int idx = t; idx < FT * FT; idx += 256) {
+        const int i = idx >> 6, k = idx & 63;
+        A[i * FP + k] = k <= i ? G[(off + i) * dp + off + k] : 0.0;
+        S[i * FP + k] = 0.0;
+    }
     if (t == 0) s_bad = 0;
     __syncthreads();
     for (int j = 0; j < FT; ++j) {
-        if (t == 0) {
-            double v = A[j * FP + j];
-            if (!(v > 0.0) || !isfinite(v)) {
-                s_bad = 1;
-                v = 1.0;
-            }
-            A[j * FP + j] = sqrt(v);
+        double ajj = A[j * FP + j];
+        if (!(ajj > 0.0) || !isfinite(ajj)) {
+            if (t == 0) s_bad = 1;
+            ajj = 1.0;
+        }
+        const double cjj = sqrt(ajj), rcjj = 1.0 / cjj;
+        if (t < FT) {
+            if (t > j) A[t * FP + j] *= rcjj;
+            else S[j * FP + t] = (t == j) ? rcjj : -S[j * FP + t] * rcjj;
         }
         __syncthreads();
-        if (t > j && t < FT) A[t * FP + j] /= A[j * FP + j];
-        __syncthreads();
-        for (int idx = t; idx < FT * FT; idx += 256) {
-            const int i = idx / FT, k = idx % FT;
-            if (k > j && k <= i) A[i * FP + k] -= A[i * FP + j] * A[k * FP + j];
+        if (ri > j) {
+            const double cij = A[ri * FP + j];
+            for (int k = j + 1 + q; k <= ri; k += 4) A[ri * FP + k] -= cij * A[k * FP + j];
+            for (int c = q; c <= j; c += 4) S[ri * FP + c] += cij * S[j * FP + c];
         }
         __syncthreads();
     }
     for (int idx = t; idx < FT * FT; idx += 256) {
-        const int i = idx / FT, k = idx % FT;
-        blk[i * dp + k] = (k <= i) ? A[i * FP + k] : 0.0;
+        const int i = idx >> 6, k = idx & 63;
+        C[(off + i) * dp + off + k] = k < i ? A[i * FP + k] : (k == i ? sqrt(A[i * FP + i]) : 0.0);
+        X[(off + i) * dp + off + k] = k <= i ? S[i * FP + k] : 0.0;
     }
     if (t == 0 && s_bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
 }
 
-// panel below the diagonal block: G[ib][kb] <- G[ib][kb] C^-T, C = G[kb][kb]
-__global__ __launch_bounds__(64) void trsm_panel_kernel(double *G, int64_t dp, int kb) {
-    __shared__ double C[FT * FP];
-    __shared__ double X[FT * FP];
-    const int t = threadIdx.x;
-    const int ib = kb + 1 + blockIdx.x;
-    const double *cblk = G + (int64_t)kb * FT * dp + (int64_t)kb * FT;
-    double *xblk = G + (int64_t)ib * FT * dp + (int64_t)kb * FT;
-    for (int idx = t; idx < FT * FT; idx += 64) {
-        C[(idx / FT) * FP + idx % FT] = cblk[(idx / FT) * dp + idx % FT];
-        X[(idx / FT) * FP + idx % FT] = xblk[(idx / FT) * dp + idx % FT];
-    }
-    __syncthreads();
-    // row t: x C^T = b  ->  x_j = (b_j - sum_{k<j} x_k C[j][k]) / C[j][j]
-    for (int j = 0; j < FT; ++j) {
-        double s = X[t * FP + j];
-        for (int k = 0; k < j; ++k) s -= X[t * FP + k] * C[j * FP + k];
-        X[t * FP + j] = s / C[j * FP + j];
-    }
-    __syncthreads();
-    for (int idx = t; idx < FT * FT; idx += 64) xblk[(idx / FT) * dp + idx % FT] = X[(idx / FT) * FP + idx % FT];
-}
+// C (M x N) = beta C + alpha sum_k A[i][k] op(B)[k][j], op(B)[k][j] = B[j][k]
+// (bnn = 0) or B[k][j] (bnn = 1); M, N, K multiples of 64.  kmode skips k
+// blocks where a triangular operand is zero: 1 A lower (k < 64 (ib+1)), 2 the
+// B rows lower (k < 64 (jb+1), bnn = 0), 3 B lower (k >= 64 jb, bnn = 1).  lower:
+// only the output tiles on or below the diagonal (grid.x enumerates them).
+struct DGemm {
+    const double *A;
+    int64_t lda;
+    const double *B;
+    int64_t ldb;
+    double *C;
+    int64_t ldc;
+    int M, N, K, bnn, kmode, lower;
+    double alpha, beta;
+};
 
-// acc (4 x 4 per thread of a 64 x 64 tile) += A(64 x kdim) . op(B), where
-// op(B)[k][c] = B[c][k] (b_trans) or B[k][c]
-__device__ void tile_mac(const double *A, int64_t lda, const double *B, int64_t ldb, bool b_trans,
-                         int kdim, double acc[4][4], double *sA, double *sB) {
-    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-    for (int k0 = 0; k0 < kdim; k0 += KC) {
+__global__ __launch_bounds__(256) void dgemm_kernel(DGemm g) {
+    int ib, jb;
+    if (g.lower) {
+        const int64_t x = blockIdx.x;
+        int64_t a = (int64_t)((sqrt(8.0 * (double)x + 1.0) - 1.0) * 0.5);
+        while (a * (a + 1) / 2 > x) --a;
+        while ((a + 1) * (a + 2) / 2 <= x) ++a;
+        ib = (int)a;
+        jb = (int)(x - a * (a + 1) / 2);
+    } else {
+        ib = blockIdx.y;
+        jb = blockIdx.x;
+    }
+    int klo = 0, khi = g.K;
+    if (g.kmode == 1) khi = min(g.K, FT * (ib + 1));
+    if (g.kmode == 2) khi = min(g.K, FT * (jb + 1));
+    if (g.kmode == 3) klo = FT * jb;
+    __shared__ double As[FT * GS];
+    __shared__ double Bs[FT * GS];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int qr = w >> 1, qc = w & 1;
+    doublex4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = doublex4{0.0, 0.0, 0.0, 0.0};
+    const double *Ab = g.A + (int64_t)FT * ib * g.lda;
+    for (int k0 = klo; k0 < khi; k0 += GK) {
         __syncthreads();
-        for (int idx = t; idx < FT * KC; idx += 256) {
-            const int r = idx / KC, kk = idx % KC;
-            sA[r * (KC + 1) + kk] = A[(int64_t)r * lda + k0 + kk];
-            if (b_trans) {
-                sB[r * (KC + 1) + kk] = B[(int64_t)r * ldb + k0 + kk];
-            } else {
-                const int kk2 = idx / FT, c = idx % FT;
-                sB[c * (KC + 1) + kk2] = B[(int64_t)(k0 + kk2) * ldb + c];
-            }
+        {   // A: 64 rows x 16 k, 4 consecutive k per thread
+            const int row = t >> 2, kk = (t & 3) * 4;
+            const double *src = Ab + (int64_t)row * g.lda + k0 + kk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) As[row * GS + kk + q] = src[q];
+        }
+        if (!g.bnn) {
+            const int row = t >> 2, kk = (t & 3) * 4;
+            const double *src = g.B + ((int64_t)FT * jb + row) * g.ldb + k0 + kk;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Bs[row * GS + kk + q] = src[q];
+        } else {
+            const int kk = t >> 4, j = (t & 15) * 4;
+            const double *src = g.B + (int64_t)(k0 + kk) * g.ldb + (int64_t)FT * jb + j;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Bs[(j + q) * GS + kk] = src[q];
         }
         __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < KC; ++kk) {
-            double a[4], b[4];
+        // lane l supplies A[l % 16][k] and B[k][l % 16] with k = 4 s + l / 16
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a[q] = sA[(ty * 4 + q) * (KC + 1) + kk];
-                b[q] = sB[(tx * 4 + q) * (KC + 1) + kk];
+        for (int s = 0; s < GK / 4; ++s) {
+            double av[2], bv[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) av[a] = As[(32 * qr + 16 * a + (lane & 15)) * GS + 4 * s + (lane >> 4)];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) bv[b] = Bs[(32 * qc + 16 * b + (lane & 15)) * GS + 4 * s + (lane >> 4)];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+    }
+    // register v of lane l holds D[l / 16 + 4 v][l % 16] of each 16 x 16 block
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = (int64_t)FT * ib + 32 * qr + 16 * a + (lane >> 4) + 4 * v;
+                const int64_t col = (int64_t)FT * jb + 32 * qc + 16 * b + (lane & 15);
+                double *c = g.C + row * g.ldc + col;
+                const double r = g.alpha * acc[a][b][v];
+                *c = g.beta != 0.0 ? fma(g.beta, *c, r) : r;
             }
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[p][q] = fma(a[p], b[q], acc[p][q]);
-        }
-    }
-}
-
-// trailing update G[ib][jb] -= G[ib][kb] G[jb][kb]^T for kb < jb <= ib < Nb
-__global__ __launch_bounds__(256) void syrk_update_kernel(double *G, int64_t dp, int kb, int Nb) {
-    __shared__ double sA[FT * (KC + 1)];
-    __shared__ double sB[FT * (KC + 1)];
-    const int64_t x = blockIdx.x;
-    int64_t a = (int64_t)((sqrt(8.0 * (double)x + 1.0) - 1.0) * 0.5);
-    while (a * (a + 1) / 2 > x) --a;
-    while ((a + 1) * (a + 2) / 2 <= x) ++a;
-    const int ib = kb + 1 + (int)a;
-    const int jb = kb + 1 + (int)(x - a * (a + 1) / 2);
-    if (ib >= Nb || jb > ib) return;
-    double acc[4][4] = {};
-    tile_mac(G + (int64_t)ib * FT * dp + (int64_t)kb * FT, dp, G + (int64_t)jb * FT * dp + (int64_t)kb * FT,
-             dp, true, FT, acc, sA, sB);
-    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-    double *c = G + (int64_t)ib * FT * dp + (int64_t)jb * FT;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c[(int64_t)(ty * 4 + p) * dp + tx * 4 + q] -= acc[p][q];
-}
-
-// inverse of every diagonal block of the lower factor C: Dinv[b] = C[b][b]^-1,
-// also written to X[b][b]
-__global__ __launch_bounds__(64) void trinv_diag_kernel(const double *C, int64_t dp, double *X,
-                                                        double *Dinv) {
-    __shared__ double Cs[FT * FP];
-    __shared__ double Y[FT * FP];
-    const int t = threadIdx.x, b = blockIdx.x;
-    const double *cblk = C + (int64_t)b * FT * dp + (int64_t)b * FT;
-    for (int idx = t; idx < FT * FT; idx += 64) Cs[(idx / FT) * FP + idx % FT] = cblk[(idx / FT) * dp + idx % FT];
-    __syncthreads();
-    // column t of Y = C^-1: forward substitution on e_t
-    for (int r = 0; r < FT; ++r) {
-        double s = (r == t) ? 1.0 : 0.0;
-        for (int k = 0; k < r; ++k) s -= Cs[r * FP + k] * Y[k * FP + t];
-        Y[r * FP + t] = s / Cs[r * FP + r];
-    }
-    __syncthreads();
-    double *xblk = X + (int64_t)b * FT * dp + (int64_t)b * FT;
-    double *dblk = Dinv + (int64_t)b * FT * FT;
-    for (int idx = t; idx < FT * FT; idx += 64) {
-        const double v = Y[(idx / FT) * FP + idx % FT];
-        xblk[(idx / FT) * dp + idx % FT] = v;
-        dblk[idx] = v;
-    }
-}
-
-// block row i of X = C^-1: X[i][j] = -Dinv[i] sum_{k=j}^{i-1} C[i][k] X[k][j], j < i
-__global__ __launch_bounds__(256) void trinv_row_kernel(const double *C, int64_t dp, double *X,
-                                                        const double *Dinv, int i) {
-    __shared__ double sA[FT * (KC + 1)];
-    __shared__ double sB[FT * (KC + 1)];
-    __shared__ double R[FT * FP];
-    const int j = blockIdx.x;
-    const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-    double acc[4][4] = {};
-    tile_mac(C + (int64_t)i * FT * dp + (int64_t)j * FT, dp, X + (int64_t)j * FT * dp + (int64_t)j * FT, dp,
-             false, (i - j) * FT, acc, sA, sB);
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) R[(ty * 4 + p) * FP + tx * 4 + q] = acc[p][q];
-    __syncthreads();
-    double out[4][4] = {};
-    const double *D = Dinv + (int64_t)i * FT * FT;
-    for (int k = 0; k < FT; ++k) {
-        double a[4], b[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            a[q] = D[(ty * 4 + q) * FT + k];
-            b[q] = R[k * FP + tx * 4 + q];
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) out[p][q] = fma(a[p], b[q], out[p][q]);
-    }
-    double *xblk = X + (int64_t)i * FT * dp + (int64_t)j * FT;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xblk[(int64_t)(ty * 4 + p) * dp + tx * 4 + q] = -out[p][q];
 }
 
 // L[a][b] = X[d-1-b][d-1-a] for b <= a, 0 above; tiled transpose through LDS
@@ -235,16 +216,70 @@ __global__ __launch_bounds__(256) void write_l_kernel(const double *X, int64_t d
 }
 
 struct FBufs {
-    double *G, *X, *Dinv;
+    double *G, *C, *X, *T;
 };
 
 size_t fcarve(void *ws, int64_t dp, FBufs *f) {
     Carver cv(ws);
     double *G = cv.take<double>(dp * dp);
+    double *C = cv.take<double>(dp * dp);
     double *X = cv.take<double>(dp * dp);
-    double *D = cv.take<double>(dp * FT);
-    if (f) *f = FBufs{G, X, D};
+    double *T = cv.take<double>(dp * dp);
+    if (f) *f = FBufs{G, C, X, T};
     return cv.used;
+}
+
+struct Factor {
+    FBufs f;
+    int64_t dp;
+    int32_t *dev_status;
+    hipStream_t stream;
+};
+
+int32_t gemm(const Factor &fc, const double *A, const double *B, double *Cout, int M, int N, int K,
+             int bnn, int kmode, int lower, double alpha, double beta) {
+    DGemm g{A, fc.dp, B, fc.dp, Cout, fc.dp, M, N, K, bnn, kmode, lower, alpha, beta};
+    const int mb = M / FT, nb = N / FT;
+    if (lower) {
+        hipLaunchKernelGGL(dgemm_kernel, dim3((unsigned)(mb * (mb + 1) / 2)), dim3(256), 0, fc.stream, g);
+    } else {
+        hipLaunchKernelGGL(dgemm_kernel, dim3(nb, mb), dim3(256), 0, fc.stream, g);
+    }
+    BK_LAUNCH_CHECK("dgemm_kernel");
+    return BAKRON_OK;
+}
+
+// factor and invert the diagonal block [off, off + n) of G into C and X
+int32_t recurse(const Factor &fc, int64_t off, int64_t n) {
+    const int64_t dp = fc.dp;
+    if (n == FT) {
+        hipLaunchKernelGGL(base_kernel, dim3(1), dim3(256), 0, fc.stream, fc.f.G, fc.f.C, fc.f.X, dp,
+                           off, fc.dev_status);
+        BK_LAUNCH_CHECK("base_kernel");
+        return BAKRON_OK;
+    }
+    const int64_t n1 = (n / FT / 2) * FT, n2 = n - n1;
+    int32_t st = recurse(fc, off, n1);
+    if (st != BAKRON_OK) return st;
+    auto at = [dp](double *p, int64_t r, int64_t c) { return p + r * dp + c; };
+    double *G = fc.f.G, *C = fc.f.C, *X = fc.f.X, *T = fc.f.T;
+    // C21 = G21 X11^T (X11 lower: the rows of X11 end at the output column block)
+    st = gemm(fc, at(G, off + n1, off), at(X, off, off), at(C, off + n1, off), (int)n2, (int)n1,
+              (int)n1, 0, 2, 0, 1.0, 0.0);
+    if (st != BAKRON_OK) return st;
+    // G22 -= C21 C21^T, lower tiles
+    st = gemm(fc, at(C, off + n1, off), at(C, off + n1, off), at(G, off + n1, off + n1), (int)n2,
+              (int)n2, (int)n1, 0, 0, 1, -1.0, 1.0);
+    if (st != BAKRON_OK) return st;
+    st = recurse(fc, off + n1, n2);
+    if (st != BAKRON_OK) return st;
+    // T = C21 X11 (X11 lower: rows k >= the output column block), X21 = -X22 T (X22 lower)
+    st = gemm(fc, at(C, off + n1, off), at(X, off, off), at(T, off + n1, off), (int)n2, (int)n1,
+              (int)n1, 1, 3, 0, 1.0, 0.0);
+    if (st != BAKRON_OK) return st;
+    st = gemm(fc, at(X, off + n1, off + n1), at(T, off + n1, off), at(X, off + n1, off), (int)n2,
+              (int)n1, (int)n2, 1, 1, 0, -1.0, 0.0);
+    return st;
 }
 
 }  // namespace
@@ -271,34 +306,17 @@ extern "C" int32_t bakron_factor(const float *H, int64_t d, float *L, int32_t *d
     int32_t st = check_device();
     if (st != BAKRON_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    const int64_t dp = round_up(d, FT);
-    const int Nb = (int)(dp / FT);
-    FBufs f;
-    fcarve(ws, dp, &f);
-    hipLaunchKernelGGL(load_reversed_kernel, dim3(2048), dim3(256), 0, stream, H, d, f.G, dp);
+    Factor fc;
+    fc.dp = round_up(d, FT);
+    fc.dev_status = dev_status;
+    fc.stream = stream;
+    fcarve(ws, fc.dp, &fc.f);
+    hipLaunchKernelGGL(load_reversed_kernel, dim3(2048), dim3(256), 0, stream, H, d, fc.f.G, fc.dp);
     BK_LAUNCH_CHECK("load_reversed_kernel");
-    for (int kb = 0; kb < Nb; ++kb) {
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, stream, f.G, dp, kb, dev_status);
-        BK_LAUNCH_CHECK("chol_diag_kernel");
-        const int below = Nb - kb - 1;
-        if (below > 0) {
-            hipLaunchKernelGGL(trsm_panel_kernel, dim3(below), dim3(64), 0, stream, f.G, dp, kb);
-            BK_LAUNCH_CHECK("trsm_panel_kernel");
-            const int64_t tiles = (int64_t)below * (below + 1) / 2;
-            hipLaunchKernelGGL(syrk_update_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, f.G, dp,
-                               kb, Nb);
-            BK_LAUNCH_CHECK("syrk_update_kernel");
-        }
-    }
-    // C^-1, block row by block row
-    hipLaunchKernelGGL(trinv_diag_kernel, dim3(Nb), dim3(64), 0, stream, f.G, dp, f.X, f.Dinv);
-    BK_LAUNCH_CHECK("trinv_diag_kernel");
-    for (int i = 1; i < Nb; ++i) {
-        hipLaunchKernelGGL(trinv_row_kernel, dim3(i), dim3(256), 0, stream, f.G, dp, f.X, f.Dinv, i);
-        BK_LAUNCH_CHECK("trinv_row_kernel");
-    }
+    st = recurse(fc, 0, fc.dp);
+    if (st != BAKRON_OK) return st;
     const unsigned tl = (unsigned)((d + FT - 1) / FT);
-    hipLaunchKernelGGL(write_l_kernel, dim3(tl, tl), dim3(256), 0, stream, f.X, dp, d, L);
+    hipLaunchKernelGGL(write_l_kernel, dim3(tl, tl), dim3(256), 0, stream, fc.f.X, fc.dp, d, L);
     BK_LAUNCH_CHECK("write_l_kernel");
     return BAKRON_OK;
 }
