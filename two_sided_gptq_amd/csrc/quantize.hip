@@ -664,6 +664,7 @@ struct BandArgs {
     float *C;
     int64_t lda, ldb, ldc;
     int mode, K, L, H, M, N, rlo, subtract;
+    int rows;  // output-tile rows of the launch (the grid pads them to a multiple of 8)
 };
 
 __device__ inline bool band_tile(const BandArgs &g, int bx, int by, int &ci, int &cj,
@@ -697,10 +698,17 @@ __device__ inline bool band_tile(const BandArgs &g, int bx, int by, int &ci, int
 // contiguous float4 from LDS.  The next K block is prefetched into registers
 // while the current one is multiplied.
 __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
-    // longest tiles first: the K depth grows with the band offset in every
-    // mode and with the row in the second products, so those run backwards
-    const int bx = gridDim.x - 1 - blockIdx.x;
-    const int by = (g.mode == 1 || g.mode == 3) ? gridDim.y - 1 - blockIdx.y : blockIdx.y;
+    // Workgroups go to the 8 XCDs round-robin by linear id; XCD x takes the
+    // rows y = x (mod 8), a whole row at a time, so the operand block that a
+    // row shares (its A rows) is fetched into one XCD's L2 only.  Longest
+    // tiles first: the K depth grows with the band offset in every mode and
+    // with the row in the second products, so those run backwards.
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x, slot = lin >> 3;
+    const int gy = (lin & 7) + 8 * (slot / (int)gridDim.x);
+    const int gx = slot % (int)gridDim.x;
+    if (gy >= g.rows) return;
+    const int bx = gridDim.x - 1 - gx;
+    const int by = (g.mode == 1 || g.mode == 3) ? g.rows - 1 - gy : gy;
     int ci, cj, klo, khi;
     if (!band_tile(g, bx, by, ci, cj, klo, khi)) return;
     __shared__ __align__(16) float As[TB * GP];
@@ -1153,12 +1161,16 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_
                 g1 = BandArgs{b.LBp, b.Ebuf, b.Tbuf, mp, mp, np, 2, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
                 g2 = BandArgs{b.Tbuf, b.LAp, b.Wp, np, np, np, 3, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
             }
+            g1.rows = p1.rows;
+            g2.rows = p2.rows;
             if (p1.rows > 0) {
-                hipLaunchKernelGGL(band_gemm_kernel, dim3(p1.cols, p1.rows), dim3(256), 0, stream, g1);
+                hipLaunchKernelGGL(band_gemm_kernel, dim3(p1.cols, (p1.rows + 7) & ~7), dim3(256), 0,
+                                   stream, g1);
                 BK_LAUNCH_CHECK("band_gemm_kernel");
             }
             if (p2.rows > 0) {
-                hipLaunchKernelGGL(band_gemm_kernel, dim3(p2.cols, p2.rows), dim3(256), 0, stream, g2);
+                hipLaunchKernelGGL(band_gemm_kernel, dim3(p2.cols, (p2.rows + 7) & ~7), dim3(256), 0,
+                                   stream, g2);
                 BK_LAUNCH_CHECK("band_gemm_kernel");
             }
             BK_MARK(2);
