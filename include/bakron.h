@@ -52,6 +52,7 @@ extern "C" {
 /* bits OR-ed into *dev_status by the kernels */
 #define BAKRON_DEV_NONFINITE 1  /* a non-finite weight or error term was met */
 #define BAKRON_DEV_NOT_PD 2     /* a non-positive pivot in bakron_factor */
+#define BAKRON_DEV_SPIN_LIMIT 4 /* a bounded wait inside a kernel gave up (results invalid) */
 
 /* base quantizer kinds (the solver is modular in the base quantizer; review
  * page abstract).  Per-row (output channel) parameters from the ORIGINAL W:
@@ -122,11 +123,19 @@ int32_t bakron_factor(const float *H, int64_t d, float *L, int32_t *dev_status,
  * Any m, n >= 1 is accepted; inside, W is handled in 64 x 64 tiles with
  * zero padding.  The result equals the raster-order naive solver up to fp32
  * rounding order (Theorem 3.2).
- * The static schedule of a solve is captured once into an executable HIP graph,
- * cached per (device, sizes, quantizer, order, every pointer argument, ws) --
- * at most 16 graphs, least recently used dropped -- and replayed on `stream`.
- * The first call with a new key pays the capture.  Not thread-safe across
- * concurrent calls that share a workspace (they race on it anyway).
+ * The static schedule of a solve (see bakron_schedule_plan) runs on two
+ * streams: `stream` carries the leaves and the band products that feed the
+ * next target diagonals; the rest of the wide recursion nodes' products runs
+ * on a side stream of the library's, forked and joined with events, while the
+ * leaves occupy few CUs.  The results do not depend on the interleaving (the
+ * plan orders every pair of steps that share data) and are the same bit for
+ * bit with and without BAKRON_FLAG_NO_GRAPH and BAKRON_FLAG_PHASE_TIMING (the
+ * latter runs the plan in order on `stream`).
+ * The schedule is captured once into an executable HIP graph, cached per
+ * (device, sizes, quantizer, order, every pointer argument, ws) -- at most 16
+ * graphs, least recently used dropped -- and replayed on `stream`.  The first
+ * call with a new key pays the capture.  Not thread-safe across concurrent
+ * calls that share a workspace (they race on it anyway).
  */
 size_t bakron_quantize_workspace_size(int64_t m, int64_t n, int32_t qkind, int32_t qbits);
 int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
@@ -137,7 +146,7 @@ int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
 
 /*
  * bakron_schedule_info -- the static schedule for an m x n solve, without
- * touching the GPU.  out[0..12]:
+ * touching the GPU.  out[0..14]:
  *   0 tile size b           1 leaf launches (tile anti-diagonals M+N-1)
  *   2 band GEMM launches    3 sequential in-kernel diagonal steps ((M+N-1)(2b-1))
  *   4 order used (1 = LA first, 2 = LB first)
@@ -153,15 +162,39 @@ int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
  *     launch of its own; the leaf of its second diagonal applies its update
  *     (up to four dense b x b x b products per tile)
  *  12 leaf launches that pull
+ *  13 of the band launches in out[2]: deferred ones (side stream)
+ *  14 useful flops of the deferred launches (part of out[10])
  * Returns BAKRON_OK or BAKRON_ERR_INVALID_ARG.
  */
 int32_t bakron_schedule_info(int64_t m, int64_t n, int32_t flags, double *out);
 
+/*
+ * bakron_schedule_plan -- the ordered steps of an m x n solve, for inspection
+ * and tests; touches no GPU.  Writes *count; with ops != NULL (cap >= *count
+ * entries of 16 int32, else BAKRON_ERR_INVALID_ARG) entry k is step k:
+ *   [0] kind: 0 leaf, 1 band product, 2 record event, 3 wait for event
+ *   [1] band: 1 = deferred (side stream); record / wait: 1 = on the side stream
+ *   [2] record / wait: event index
+ *   leaf:  [3] tile diagonal K, [4] 1 = applies the previous leaf's
+ *          two-diagonal update, 2 = computes it for the next leaf
+ *   band:  [3] K, [5] L, [6] H of the recursion node (split at K + H), [7] its
+ *          depth (selects its T buffer), [8] product (0 first, 1 second),
+ *          [9..10] diagonal range lo, hi (T diagonals for the first product,
+ *          W target diagonals for the second), then the launch grid for the
+ *          order given in flags: [11] mode, [12] first band offset, [13] offsets,
+ *          [14] first row, [15] rows (-1 when the range holds no tile).
+ * Unused fields are -1.  Returns BAKRON_OK or BAKRON_ERR_INVALID_ARG.
+ */
+int32_t bakron_schedule_plan(int64_t m, int64_t n, int32_t flags, int32_t *ops, int64_t cap,
+                             int64_t *count);
+
 /* Per-phase times (ms) of the calling thread's last bakron_quantize call made
- * with BAKRON_FLAG_PHASE_TIMING: out[0] quantizer parameters + relayout,
- * out[1] leaf kernels, out[2] band GEMM kernels, out[3] finalise, out[4] leaf
- * launches, out[5] band GEMM launches.  Returns BAKRON_ERR_INVALID_ARG if no
- * such call was made. */
+ * with BAKRON_FLAG_PHASE_TIMING (the plan run in order on one stream): out[0]
+ * quantizer parameters + relayout, out[1] leaf kernels, out[2] band GEMM
+ * kernels on the critical stream, out[3] finalise, out[4] leaf launches,
+ * out[5] critical band GEMM launches, out[6] deferred band kernels, out[7]
+ * deferred band launches.  Returns BAKRON_ERR_INVALID_ARG if no such call was
+ * made. */
 int32_t bakron_last_phase_ms(double *out);
 
 const char *bakron_status_string(int32_t status);

@@ -153,7 +153,9 @@ def test_schedule_shape(lib):
     band, pulls = _tile_recursion(127)
     assert s["leaf_launches"] == 127 and s["leaf_steps"] == 127 * 127
     assert len(band) + len(pulls) == 126          # every node of the recursion
-    assert s["band_launches"] == 2 * len(band)
+    # two products per node; a node deferring part of its work adds two more
+    assert s["band_launches"] == 2 * len(band) + s["side_launches"]
+    assert s["side_launches"] == 2 * sum(1 for (K, L, H) in band if L - H >= 16)
     assert s["pull_leaves"] == len(pulls)
     tiles = lambda K: [(I, K - I) for I in range(max(0, K - 63), min(63, K) + 1)]
     prods = sum((2 if I >= 1 else 0) + (2 if J >= 1 else 0) for K in pulls for I, J in tiles(K))

@@ -171,3 +171,38 @@ def test_graph_replay_matches_eager(bk):
                 assert np.array_equal(got[k], ref[k]), (rep, k)
             # eager work between replays
             run(W_host, False)
+
+
+@pytest.mark.parametrize("m,n,order", [(1024, 1024, 1), (1536, 1024, 2), (1024, 3008, 0)])
+def test_two_stream_modes_agree(bk, m, n, order):
+    """At sizes where wide recursion nodes defer part of their band products to
+    the side stream, the graph replay, the eager two-stream launch and the
+    timing pass (the same plan in order on one stream) give the same results
+    bit for bit, and agree with the oracle's invariants."""
+    print(f"[modes] {m}x{n} order {order}", flush=True)
+    assert bk.schedule_info(m, n, order)["side_launches"] > 0
+    W, X, Y = synth.custom(m, n, 7000 + m + n)
+    A, B, LA, LB = _factors(X, Y, m)
+    dev = torch.device("cuda:0")
+    Wd, LAd, LBd = (torch.from_numpy(a).to(dev) for a in (W, LA, LB))
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    runs = []
+    for mode in ("graph", "eager", "timing", "graph"):
+        out = bk.quantize(Wd, LAd, LBd, kind=0, bits=4, order=order, want_E=True, want_sum=True,
+                          dev_status=status, graph=(mode == "graph"), timing=(mode == "timing"))
+        torch.cuda.synchronize()
+        runs.append({k: v.cpu().numpy().copy() for k, v in out.items() if v is not None})
+    assert int(status.item()) == 0
+    for r in runs[1:]:
+        for k in runs[0]:
+            assert np.array_equal(r[k], runs[0][k]), k
+    res = runs[0]
+    s = res["scales"]
+    bad, _ = oracle.rounding_consistency(res["codes"], res["V"], res["E"], np.diag(LA), np.diag(LB),
+                                         s, np.zeros_like(s), 0, 4)
+    assert bad == 0
+    rows = np.unique(np.r_[0, 63, 64, m // 2, m - 1])
+    R = oracle.completion_residual(W, res["V"], res["E"], LA, LB, rows=rows)
+    bound = (np.abs(LB[rows, :].astype(np.float64)) @ np.abs(res["E"].astype(np.float64))) @ \
+        np.abs(LA.astype(np.float64)).T
+    assert np.max(np.abs(R) / (bound + 1e-30)) <= 1e-4

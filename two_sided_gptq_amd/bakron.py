@@ -25,7 +25,7 @@ EXPORTS = (
     "bakron_hessian_workspace_size", "bakron_hessian",
     "bakron_factor_workspace_size", "bakron_factor",
     "bakron_quantize_workspace_size", "bakron_quantize",
-    "bakron_schedule_info", "bakron_last_phase_ms",
+    "bakron_schedule_info", "bakron_schedule_plan", "bakron_last_phase_ms",
     "bakron_status_string", "bakron_last_error",
 )
 
@@ -60,6 +60,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bakron_quantize.restype = I32
     lib.bakron_schedule_info.argtypes = [I64, I64, I32, ctypes.POINTER(D)]
     lib.bakron_schedule_info.restype = I32
+    lib.bakron_schedule_plan.argtypes = [I64, I64, I32, ctypes.POINTER(I32), I64,
+                                         ctypes.POINTER(I64)]
+    lib.bakron_schedule_plan.restype = I32
     lib.bakron_last_phase_ms.argtypes = [ctypes.POINTER(D)]
     lib.bakron_last_phase_ms.restype = I32
     lib.bakron_status_string.argtypes = [I32]
@@ -158,7 +161,8 @@ def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_
 
 SCHEDULE_KEYS = ("tile", "leaf_launches", "band_launches", "leaf_steps", "order",
                  "alg_band_flops", "exec_band_flops", "F", "leaf_flops", "depth",
-                 "useful_band_flops", "pull_flops", "pull_leaves")
+                 "useful_band_flops", "pull_flops", "pull_leaves", "side_launches",
+                 "side_useful_flops")
 
 
 def schedule_info(m: int, n: int, order: int = ORDER_AUTO) -> dict:
@@ -168,11 +172,28 @@ def schedule_info(m: int, n: int, order: int = ORDER_AUTO) -> dict:
     return dict(zip(SCHEDULE_KEYS, list(buf)))
 
 
-PHASE_KEYS = ("prep_ms", "leaf_ms", "band_ms", "final_ms", "leaf_launches", "band_launches")
+PLAN_FIELDS = ("kind", "side", "ev", "K", "flags", "L", "H", "depth", "prod", "lo", "hi",
+               "mode", "olo", "cols", "rlo", "rows")
+
+
+def schedule_plan(m: int, n: int, order: int = ORDER_AUTO) -> list:
+    """The ordered steps of an m x n solve (bakron_schedule_plan), one dict each."""
+    lib = load()
+    count = ctypes.c_int64(0)
+    _check(lib.bakron_schedule_plan(m, n, order, None, 0, ctypes.byref(count)), "bakron_schedule_plan")
+    buf = (ctypes.c_int32 * (16 * count.value))()
+    _check(lib.bakron_schedule_plan(m, n, order, buf, count.value, ctypes.byref(count)),
+           "bakron_schedule_plan")
+    vals = list(buf)
+    return [dict(zip(PLAN_FIELDS, vals[16 * k:16 * k + 16])) for k in range(count.value)]
+
+
+PHASE_KEYS = ("prep_ms", "leaf_ms", "band_ms", "final_ms", "leaf_launches", "band_launches",
+              "side_ms", "side_launches")
 
 
 def last_phase_ms() -> dict:
     lib = load()
-    buf = (ctypes.c_double * 6)()
+    buf = (ctypes.c_double * len(PHASE_KEYS))()
     _check(lib.bakron_last_phase_ms(buf), "bakron_last_phase_ms")
     return dict(zip(PHASE_KEYS, list(buf)))

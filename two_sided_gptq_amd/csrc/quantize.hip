@@ -21,6 +21,8 @@
 //                                  staircase fp32-MFMA GEMMs
 //   4. finalise   sum of e^2 in a fixed order
 #include <algorithm>
+#include <climits>
+#include <cstddef>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -658,13 +660,15 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
 //   mode 1  (LA first, product 2)  W(I',J') -= sum_I LB(I',I) Tt(J',I)^T
 //   mode 2  (LB first, product 1)  S(I',J) = sum_I LB(I',I) Et(J,I)^T
 //   mode 3  (LB first, product 2)  W(I',J') -= sum_J S(I',J) LA(J',J)^T
-// Grid: x = offset along the band, y = row index (from rlo).
+// Grid: x = offset along the band (from olo), y = row index (from rlo).
 struct BandArgs {
     const float *A, *B;
     float *C;
     int64_t lda, ldb, ldc;
     int mode, K, L, H, M, N, rlo, subtract;
     int rows;  // output-tile rows of the launch (the grid pads them to a multiple of 8)
+    int olo;   // band offset of the launch's first column (a launch may cover a sub-range)
+    int cols;  // band offsets covered: olo .. olo + cols - 1
 };
 
 __device__ inline bool band_tile(const BandArgs &g, int bx, int by, int &ci, int &cj,
@@ -707,7 +711,7 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
     const int gy = (lin & 7) + 8 * (slot / (int)gridDim.x);
     const int gx = slot % (int)gridDim.x;
     if (gy >= g.rows) return;
-    const int bx = gridDim.x - 1 - gx;
+    const int bx = g.olo + gridDim.x - 1 - gx;
     const int by = (g.mode == 1 || g.mode == 3) ? g.rows - 1 - gy : gy;
     int ci, cj, klo, khi;
     if (!band_tile(g, bx, by, ci, cj, klo, khi)) return;
@@ -782,6 +786,136 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
     }
 }
 
+// Band products that run beside the leaves.  A launch has at most SIDE_WG
+// workgroups of 1024 threads, and each workgroup's LDS (four tiles' operand
+// blocks, 139 KB) keeps it alone on its CU, so a side launch never holds more
+// than SIDE_WG CUs: the leaves, one workgroup of 160 KB LDS per tile, always
+// find empty CUs.  The four 4-wave slots of a workgroup work independently,
+// like four workgroups of band_gemm_kernel.  The launch's tiles, in
+// band_gemm_kernel's grid order (row-major, longest first), go first to slot 0
+// of every workgroup, then slot 1, and so on (one tile per CU before two);
+// after its first tile a slot takes the next one from the launch's counter
+// `ctr` (zero at the start).  A slot runs each tile exactly as
+// band_gemm_kernel does, with a barrier of its own four waves (a counter in
+// LDS) in place of the workgroup barrier.  A slot barrier waits for the three
+// other waves of the slot, which run the same sequence of barriers; the wait
+// is bounded all the same, and a wait that reaches the bound sets
+// BAKRON_DEV_SPIN_LIMIT in *dev_status.
+constexpr int SIDE_WG = 160;
+constexpr int SIDE_THREADS = 1024;
+constexpr int SPIN_LIMIT = 1 << 22;
+
+__global__ __launch_bounds__(SIDE_THREADS) void band_side_kernel(BandArgs g, int *ctr,
+                                                                 int32_t *dev_status) {
+    __shared__ __align__(16) float As[4 * TB * GP];
+    __shared__ __align__(16) float Bs[4 * TB * GP];
+    __shared__ int s_arrive[4];  // arrivals at slot barriers, per slot
+    __shared__ int s_tile[4];    // next tile index, per slot
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = w >> 2, wq = w & 3;
+    const int wr = wq >> 1, wc = wq & 1;
+    const int t2 = tid & 255, lr = t2 >> 4, lc = (t2 & 15) * 4;
+    const int ntile = g.cols * g.rows;
+    const float *ap = As + q * TB * GP + (wr * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
+    const float *bp = Bs + q * TB * GP + (wc * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
+    float *as_w = As + q * TB * GP + lr * GP + lc;
+    float *bs_w = Bs + q * TB * GP + lr * GP + lc;
+    const int first = 4 * gridDim.x;  // tiles dealt before the counter is used
+    if (tid < 4) s_arrive[tid] = 0;
+    __syncthreads();  // the only barrier of the whole workgroup
+    int target = 0, stuck = 0;
+    auto slot_barrier = [&]() {
+        target += 4;
+        if (lane == 0) __hip_atomic_fetch_add(&s_arrive[q], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int spin = 0; __hip_atomic_load(&s_arrive[q], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target;
+             ++spin) {
+            if (spin >= SPIN_LIMIT) {
+                stuck = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    };
+    int t = q * gridDim.x + blockIdx.x;
+    while (t < ntile) {
+        int next = 0;
+        if (wq == 0 && lane == 0) next = first + atomicAdd(ctr, 1);  // published after this tile
+        const int gy = t / g.cols, gx = t - gy * g.cols;
+        const int bx = g.olo + g.cols - 1 - gx;
+        const int by = (g.mode == 1 || g.mode == 3) ? g.rows - 1 - gy : gy;
+        int ci, cj, klo, khi;
+        if (band_tile(g, bx, by, ci, cj, klo, khi)) {  // uniform over the slot
+            const float *Ab = g.A + (int64_t)ci * TB * g.lda + (int64_t)lr * g.lda + lc;
+            const float *Bb = g.B + (int64_t)cj * TB * g.ldb + (int64_t)lr * g.ldb + lc;
+            const int64_t sa = 16 * g.lda, sb = 16 * g.ldb;
+            float4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define BK_SLOAD(kb)                                                                 \
+    do {                                                                             \
+        const float *a_ = Ab + (kb) * TB;                                            \
+        const float *b_ = Bb + (kb) * TB;                                            \
+        ra0 = *reinterpret_cast<const float4 *>(a_);                                 \
+        ra1 = *reinterpret_cast<const float4 *>(a_ + sa);                            \
+        ra2 = *reinterpret_cast<const float4 *>(a_ + 2 * sa);                        \
+        ra3 = *reinterpret_cast<const float4 *>(a_ + 3 * sa);                        \
+        rb0 = *reinterpret_cast<const float4 *>(b_);                                 \
+        rb1 = *reinterpret_cast<const float4 *>(b_ + sb);                            \
+        rb2 = *reinterpret_cast<const float4 *>(b_ + 2 * sb);                        \
+        rb3 = *reinterpret_cast<const float4 *>(b_ + 3 * sb);                        \
+    } while (0)
+            BK_SLOAD(klo);
+            floatx16 acc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+            for (int kb = klo; kb <= khi; ++kb) {
+                slot_barrier();
+                *reinterpret_cast<float4 *>(as_w) = ra0;
+                *reinterpret_cast<float4 *>(as_w + 16 * GP) = ra1;
+                *reinterpret_cast<float4 *>(as_w + 32 * GP) = ra2;
+                *reinterpret_cast<float4 *>(as_w + 48 * GP) = ra3;
+                *reinterpret_cast<float4 *>(bs_w) = rb0;
+                *reinterpret_cast<float4 *>(bs_w + 16 * GP) = rb1;
+                *reinterpret_cast<float4 *>(bs_w + 32 * GP) = rb2;
+                *reinterpret_cast<float4 *>(bs_w + 48 * GP) = rb3;
+                slot_barrier();
+                if (kb < khi) BK_SLOAD(kb + 1);
+#pragma unroll
+                for (int s4 = 0; s4 < 8; ++s4) {
+                    const float4 av = *reinterpret_cast<const float4 *>(ap + 4 * s4);
+                    const float4 bv = *reinterpret_cast<const float4 *>(bp + 4 * s4);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
+                }
+            }
+#undef BK_SLOAD
+            const int col = lane & 31;
+            float *cb = g.C + (int64_t)(ci * TB + wr * 32 + 4 * (lane >> 5)) * g.ldc +
+                        (int64_t)cj * TB + wc * 32 + col;
+            if (g.subtract) {
+                float old[16];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) old[v] = cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc] = old[v] - acc[v];
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc] = acc[v];
+            }
+        }
+        // every wave of the slot has read s_tile[q] and finished its LDS reads
+        // of this tile; then the next index is published
+        slot_barrier();
+        if (wq == 0 && lane == 0) s_tile[q] = next;
+        slot_barrier();
+        t = s_tile[q];
+    }
+    if (stuck && lane == 0 && dev_status) atomicOr(dev_status, BAKRON_DEV_SPIN_LIMIT);
+}
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int *p, int n) {
+    for (int k = blockIdx.x * 256 + threadIdx.x; k < n; k += gridDim.x * 256) p[k] = 0;
+}
+
 // ----------------------------------------------------------------- finalise
 __global__ __launch_bounds__(256) void sumsq_partial_kernel(const float *__restrict__ x,
                                                             int64_t count, double *partial) {
@@ -821,22 +955,23 @@ struct Node {
     int leaf;  // 1: leaf(K); 0: band(K, L, H)
     int flags;  // leaf only: LEAF_PUSH / LEAF_PULL (two-diagonal nodes run inside the leaves)
     int K, L, H;
+    int depth;  // band only: recursion depth (the top node is 0); selects its T buffer
 };
 
-void build_nodes(int K, int L, std::vector<Node> &out) {
+void build_nodes(int K, int L, std::vector<Node> &out, int depth = 0) {
     if (L == 1) {
-        out.push_back({1, 0, K, 1, 0});
+        out.push_back({1, 0, K, 1, 0, depth});
         return;
     }
     if (L == 2) {  // leaf(K), band(K, 2, 1), leaf(K+1): the band runs inside the two leaves
-        out.push_back({1, LEAF_PUSH, K, 1, 0});
-        out.push_back({1, LEAF_PULL, K + 1, 1, 0});
+        out.push_back({1, LEAF_PUSH, K, 1, 0, depth});
+        out.push_back({1, LEAF_PULL, K + 1, 1, 0, depth});
         return;
     }
     const int H = L / 2;  // split of the range [K, K+L) at K + floor(L/2)
-    build_nodes(K, H, out);
-    out.push_back({0, 0, K, L, H});
-    build_nodes(K + H, L - H, out);
+    build_nodes(K, H, out, depth + 1);
+    out.push_back({0, 0, K, L, H, depth});
+    build_nodes(K + H, L - H, out, depth + 1);
 }
 
 int depth_of(int L) {
@@ -872,52 +1007,160 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
     p2.cols = L - H;
 }
 
-// Flops of the band-GEMM launches of one order (host mirror of band_tile):
-// exec counts every dense 64 x 64 x 64 tile step; useful leaves out the zero
-// half of a triangular diagonal factor block (LA(J,J) or LB(I,I)).
+// ------------------------------------------------------------------- plan
+// The order of a solve's work on two streams.  The critical stream runs the
+// leaves in diagonal order and, for every band node, the products that feed
+// its first target diagonals.  A node whose right part spans R = L - H >=
+// SIDE_MIN_R diagonals keeps only the targets K + H .. a - 1, a = K + H +
+// (R >> SIDE_SHIFT), critical: its first product over the T diagonals from a
+// on and its second product over the targets from a on go to the side stream.
+// They are forked by events once their inputs exist (the sources are final
+// when the node starts; the second product also reads the critical part of T)
+// and joined before the first critical step that updates or reads their
+// targets: the leaf of diagonal a, or a band node whose targets reach a.  So
+// the deferred products run while the leaves of K + H .. a - 1 hold a few CUs.
+// Nodes keep T in one buffer per recursion depth, so a deferred product shares
+// no T tile with the nodes that run meanwhile.  On one stream the same plan
+// gives the same results bit for bit.
+constexpr int OP_LEAF = 0, OP_BAND = 1, OP_RECORD = 2, OP_WAIT = 3;
+constexpr int SIDE_MIN_R = 16;
+constexpr int SIDE_SHIFT = 2;
+
+struct Op {
+    int kind;
+    int side;  // OP_BAND: deferred product; OP_RECORD / OP_WAIT: 1 = on the side stream
+    int ev;    // OP_RECORD / OP_WAIT: event index
+    Node nd;   // OP_LEAF / OP_BAND
+    int prod;  // OP_BAND: 0 = first product (T diagonals lo .. hi-1), 1 = second (targets lo .. hi-1)
+    int lo, hi;
+};
+
+struct Plan {
+    std::vector<Op> ops;
+    int events = 0;
+};
+
+Plan build_plan(int M, int N) {
+    Plan pl;
+    std::vector<Node> nodes;
+    build_nodes(0, M + N - 1, nodes);
+    std::vector<std::pair<int, int>> pending;  // (first target diagonal, completion event)
+    auto join = [&](int upto) {  // the critical stream waits for deferred targets below upto
+        for (size_t k = 0; k < pending.size();) {
+            if (pending[k].first < upto) {
+                pl.ops.push_back(Op{OP_WAIT, 0, pending[k].second, Node{}, 0, 0, 0});
+                pending.erase(pending.begin() + (std::ptrdiff_t)k);
+            } else {
+                ++k;
+            }
+        }
+    };
+    auto band = [&](const Node &nd, int side, int prod, int lo, int hi) {
+        pl.ops.push_back(Op{OP_BAND, side, -1, nd, prod, lo, hi});
+    };
+    auto fork = [&](int ev) {
+        pl.ops.push_back(Op{OP_RECORD, 0, ev, Node{}, 0, 0, 0});
+        pl.ops.push_back(Op{OP_WAIT, 1, ev, Node{}, 0, 0, 0});
+    };
+    for (const Node &nd : nodes) {
+        if (nd.leaf) {
+            join(nd.K + 1);
+            pl.ops.push_back(Op{OP_LEAF, 0, -1, nd, 0, 0, 0});
+            continue;
+        }
+        const int R = nd.L - nd.H, end = nd.K + nd.L;
+        const int keep = R >= SIDE_MIN_R ? (R >> SIDE_SHIFT) : R;
+        if (keep < R) {
+            const int a = nd.K + nd.H + keep;
+            const int e1 = pl.events++, e3 = pl.events++;
+            band(nd, 0, 0, nd.K, a);
+            join(a);
+            band(nd, 0, 1, nd.K + nd.H, a);
+            fork(e1);  // after the critical products: the deferred ones run beside the next leaves
+            band(nd, 1, 0, a, end);
+            band(nd, 1, 1, a, end);
+            pl.ops.push_back(Op{OP_RECORD, 1, e3, Node{}, 0, 0, 0});
+            pending.push_back({a, e3});
+        } else {
+            band(nd, 0, 0, nd.K, end);
+            join(end);
+            band(nd, 0, 1, nd.K + nd.H, end);
+        }
+    }
+    join(INT_MAX);
+    return pl;
+}
+
+// Launch geometry of one band op of the plan; false when it holds no tile.
+// Grid column o of a product covers band diagonal base + o; a row r meets the
+// columns lo .. hi-1 when the tile's other index, diagonal - r, can lie in
+// 0 .. X-1.
+bool band_geometry(const Op &op, int order, int M, int N, int &mode, int &olo, int &cols,
+                   int &rlo, int &rows) {
+    Launch p1, p2;
+    band_launches(order, op.nd.K, op.nd.L, op.nd.H, M, N, p1, p2);
+    const Launch &p = op.prod ? p2 : p1;
+    mode = p.mode;
+    olo = op.lo - (op.prod ? op.nd.K + op.nd.H : op.nd.K);
+    cols = op.hi - op.lo;
+    const int X = (mode == 2) ? M : N;
+    rlo = std::max(p.rlo, op.lo - X + 1);
+    rows = std::min(p.rlo + p.rows - 1, op.hi - 1) - rlo + 1;
+    return cols > 0 && rows > 0;
+}
+
+
+// Flops of the band-GEMM launches of one order (host mirror of band_tile),
+// over the plan's band ops: exec counts every dense 64 x 64 x 64 tile step;
+// useful leaves out the zero half of a triangular diagonal factor block (LA(J,J)
+// or LB(I,I)).  The side_* fields count the deferred products alone.
 struct BandCount {
     double exec, useful;
     int launches;
+    double side_exec, side_useful;
+    int side_launches;
 };
 
-BandCount band_flops(int order, int M, int N) {
-    std::vector<Node> nodes;
-    build_nodes(0, M + N - 1, nodes);
-    double full = 0, diag = 0;
-    int launches = 0;
-    for (const Node &nd : nodes) {
-        if (nd.leaf) continue;
-        Launch p[2];
-        band_launches(order, nd.K, nd.L, nd.H, M, N, p[0], p[1]);
-        for (int s = 0; s < 2; ++s) {
-            if (p[s].rows <= 0) continue;
-            ++launches;
-            for (int y = 0; y < p[s].rows; ++y)
-                for (int x = 0; x < p[s].cols; ++x) {
-                    const int K = nd.K, H = nd.H, row = p[s].rlo + y, o = x;
-                    int lo, hi, fac;  // fac: k block holding the factor's diagonal block
-                    if (p[s].mode == 0) {
-                        const int Jp = K - row + o;
-                        if (Jp < 0 || Jp >= N) continue;
-                        lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1 - row); fac = Jp;
-                    } else if (p[s].mode == 2) {
-                        const int Ip = K - row + o;
-                        if (Ip < 0 || Ip >= M) continue;
-                        lo = std::max(0, K - row); hi = std::min(Ip, K + H - 1 - row); fac = Ip;
-                    } else {
-                        const int Jp = K + H + o - row;
-                        if (Jp < 0 || Jp >= N) continue;
-                        if (p[s].mode == 1) { lo = std::max(0, K - Jp); hi = std::min(row, K + H - 1); fac = row; }
-                        else { lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1); fac = Jp; }
-                    }
-                    if (hi < lo) continue;
-                    full += hi - lo + 1;
-                    if (fac >= lo && fac <= hi) diag += 1;
+BandCount band_flops(const Plan &pl, int order, int M, int N) {
+    BandCount c{};
+    const double tile = 2.0 * TB * TB * TB, dtile = 2.0 * TB * TB * (TB + 1) / 2;
+    for (const Op &op : pl.ops) {
+        int mode, olo, cols, rlo, rows;
+        if (op.kind != OP_BAND || !band_geometry(op, order, M, N, mode, olo, cols, rlo, rows)) continue;
+        const int K = op.nd.K, H = op.nd.H;
+        double full = 0, diag = 0;
+        for (int row = rlo; row < rlo + rows; ++row)
+            for (int o = olo; o < olo + cols; ++o) {
+                int lo, hi, fac;  // fac: k block holding the factor's diagonal block
+                if (mode == 0) {
+                    const int Jp = K - row + o;
+                    if (Jp < 0 || Jp >= N) continue;
+                    lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1 - row); fac = Jp;
+                } else if (mode == 2) {
+                    const int Ip = K - row + o;
+                    if (Ip < 0 || Ip >= M) continue;
+                    lo = std::max(0, K - row); hi = std::min(Ip, K + H - 1 - row); fac = Ip;
+                } else {
+                    const int Jp = K + H + o - row;
+                    if (Jp < 0 || Jp >= N) continue;
+                    if (mode == 1) { lo = std::max(0, K - Jp); hi = std::min(row, K + H - 1); fac = row; }
+                    else { lo = std::max(0, K - row); hi = std::min(Jp, K + H - 1); fac = Jp; }
                 }
+                if (hi < lo) continue;
+                full += hi - lo + 1;
+                if (fac >= lo && fac <= hi) diag += 1;
+            }
+        const double ex = full * tile, us = (full - diag) * tile + diag * dtile;
+        c.exec += ex;
+        c.useful += us;
+        c.launches += 1;
+        if (op.side) {
+            c.side_exec += ex;
+            c.side_useful += us;
+            c.side_launches += 1;
         }
     }
-    const double tile = 2.0 * TB * TB * TB;
-    return BandCount{full * tile, (full - diag) * tile + diag * (2.0 * TB * TB * (TB + 1) / 2), launches};
+    return c;
 }
 
 // Two-diagonal nodes: every leaf that pushes runs up to two products per
@@ -986,6 +1229,8 @@ struct ShapeInfo {
     double pull_flops;
     int pull_leaves;
     int auto_order;
+    Plan plan;
+    int side_ops;     // deferred products of the plan (one tile counter each)
 };
 
 std::mutex g_shape_mu;
@@ -997,26 +1242,33 @@ const ShapeInfo &shape_info(int M, int N) {
     auto it = g_shapes.find(key);
     if (it != g_shapes.end()) return it->second;
     ShapeInfo s{};
-    s.band[1] = band_flops(BAKRON_ORDER_LA_FIRST, M, N);
-    s.band[2] = band_flops(BAKRON_ORDER_LB_FIRST, M, N);
+    s.plan = build_plan(M, N);
+    s.band[1] = band_flops(s.plan, BAKRON_ORDER_LA_FIRST, M, N);
+    s.band[2] = band_flops(s.plan, BAKRON_ORDER_LB_FIRST, M, N);
     pull_counts(M, N, &s.pull_flops, &s.pull_leaves);
     s.auto_order = s.band[2].exec < s.band[1].exec ? BAKRON_ORDER_LB_FIRST : BAKRON_ORDER_LA_FIRST;
+    s.side_ops = 0;
+    for (const Op &op : s.plan.ops) s.side_ops += op.kind == OP_BAND && op.side;
     return g_shapes.emplace(key, s).first->second;
 }
 
 thread_local bool g_phase_valid = false;
-thread_local double g_phase_ms[6];
+thread_local double g_phase_ms[8];
 
 struct Buffers {
     float *Wp, *Ebuf, *Tbuf, *LAp, *LBp, *sc, *zp, *Cd, *Cr;
     double *partial;
+    int *ctr;  // tile counters of the deferred products
+    int nctr;
 };
 
+// T has one mp x np slab per recursion depth.
 size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     Carver cv(ws);
+    const int slabs = depth_of((int)(mp / TB + np / TB - 1));
     float *Wp = cv.take<float>(mp * np);
     float *Eb = cv.take<float>(mp * np);
-    float *Tb = cv.take<float>(mp * np);
+    float *Tb = cv.take<float>(mp * np * slabs);
     float *LAp = cv.take<float>(np * np);
     float *LBp = cv.take<float>(mp * mp);
     float *sc = cv.take<float>(mp);
@@ -1024,7 +1276,9 @@ size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     double *part = cv.take<double>(NPART);
     float *Cd = cv.take<float>(mp * np);
     float *Cr = cv.take<float>(mp * np);
-    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part};
+    const int nctr = std::max(1, shape_info((int)(mp / TB), (int)(np / TB)).side_ops);
+    int *ctr = cv.take<int>(nctr);
+    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part, ctr, nctr};
     return cv.used;
 }
 
@@ -1070,6 +1324,44 @@ extern "C" int32_t bakron_schedule_info(int64_t m, int64_t n, int32_t flags, dou
     out[10] = si.band[order].useful;
     out[11] = si.pull_flops;
     out[12] = si.pull_leaves;
+    out[13] = si.band[order].side_launches;
+    out[14] = si.band[order].side_useful;
+    return BAKRON_OK;
+}
+
+extern "C" int32_t bakron_schedule_plan(int64_t m, int64_t n, int32_t flags, int32_t *ops,
+                                        int64_t cap, int64_t *count) {
+    clear_error();
+    BK_REQUIRE(count != nullptr, "count is NULL");
+    BK_REQUIRE(m >= 1 && n >= 1 && m <= MAX_DIM && n <= MAX_DIM, "bad shape %lld x %lld",
+               (long long)m, (long long)n);
+    const int M = (int)(round_up(m, TB) / TB), N = (int)(round_up(n, TB) / TB);
+    const ShapeInfo &si = shape_info(M, N);
+    int order = flags & BAKRON_ORDER_MASK;
+    if (order == BAKRON_ORDER_AUTO || order == 3) order = si.auto_order;
+    *count = (int64_t)si.plan.ops.size();
+    BK_REQUIRE(ops == nullptr || cap >= *count, "ops holds %lld entries, the plan has %lld",
+               (long long)cap, (long long)*count);
+    if (!ops) return BAKRON_OK;
+    for (size_t k = 0; k < si.plan.ops.size(); ++k) {
+        const Op &op = si.plan.ops[k];
+        int32_t *o = ops + 16 * k;
+        for (int f = 0; f < 16; ++f) o[f] = -1;
+        o[0] = op.kind;
+        o[1] = op.side;
+        o[2] = op.ev;
+        if (op.kind == OP_LEAF) {
+            o[3] = op.nd.K;
+            o[4] = op.nd.flags;
+        } else if (op.kind == OP_BAND) {
+            o[3] = op.nd.K; o[5] = op.nd.L; o[6] = op.nd.H; o[7] = op.nd.depth;
+            o[8] = op.prod; o[9] = op.lo; o[10] = op.hi;
+            int mode, olo, cols, rlo, rows;
+            if (band_geometry(op, order, M, N, mode, olo, cols, rlo, rows)) {
+                o[11] = mode; o[12] = olo; o[13] = cols; o[14] = rlo; o[15] = rows;
+            }
+        }
+    }
     return BAKRON_OK;
 }
 
@@ -1077,7 +1369,7 @@ extern "C" int32_t bakron_last_phase_ms(double *out) {
     clear_error();
     BK_REQUIRE(out != nullptr, "out is NULL");
     BK_REQUIRE(g_phase_valid, "no timed bakron_quantize call on this thread");
-    for (int k = 0; k < 6; ++k) out[k] = g_phase_ms[k];
+    for (int k = 0; k < 8; ++k) out[k] = g_phase_ms[k];
     return BAKRON_OK;
 }
 
@@ -1096,9 +1388,13 @@ struct Solve {
     Buffers b;
 };
 
-// Enqueues the whole solve on `stream`.  With `marks`, records an event after
-// each phase (-1 start, 0 prep, 1 leaf, 2 band node, 3 finalise).
-int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_t> *evs,
+// Enqueues the whole solve.  With `side` (and `sync`, the plan's events),
+// deferred band products run on `side`, forked from and joined into `stream`;
+// without, the plan runs in order on `stream`.  With `evs`, records an event
+// after each step (-1 start, 0 prep, 1 leaf, 2 band product, 3 finalise,
+// 4 deferred band product).
+int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
+                      const std::vector<hipEvent_t> *sync, std::vector<hipEvent_t> *evs,
                       std::vector<int> *ev_phase) {
     auto mark = [&](int phase) -> int32_t {
         if (!evs) return BAKRON_OK;
@@ -1136,11 +1432,20 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_
 
     LeafArgs la{b.Wp, b.Ebuf, b.LAp, b.LBp, b.sc, b.zp, mp, np, M, N, sv.order, sv.qmin, sv.qmax,
                 sv.codes, sv.V, sv.E, m, n, sv.dev_status, b.Cd, b.Cr};
-    std::vector<Node> nodes;
-    nodes.reserve(2 * (M + N));
-    build_nodes(0, M + N - 1, nodes);
-    for (const Node &nd : nodes) {
-        if (nd.leaf) {
+    const Plan &plan = shape_info(M, N).plan;
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, stream, b.ctr, b.nctr);
+    BK_LAUNCH_CHECK("zero_i32_kernel");
+    int side_k = 0;
+    for (const Op &op : plan.ops) {
+        if (op.kind == OP_RECORD || op.kind == OP_WAIT) {
+            if (!side) continue;
+            hipStream_t st = op.side ? side : stream;
+            if (op.kind == OP_RECORD) BK_HIP_CHECK(hipEventRecord((*sync)[op.ev], st));
+            else BK_HIP_CHECK(hipStreamWaitEvent(st, (*sync)[op.ev], 0));
+            continue;
+        }
+        const Node &nd = op.nd;
+        if (op.kind == OP_LEAF) {
             const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
             if (sv.qkind == BAKRON_Q_ASYM)
                 hipLaunchKernelGGL(leaf_kernel<true>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream,
@@ -1150,31 +1455,30 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, std::vector<hipEvent_
                                    la, nd.K, nd.flags);
             BK_LAUNCH_CHECK("leaf_kernel");
             BK_MARK(1);
-        } else {
-            Launch p1, p2;
-            band_launches(sv.order, nd.K, nd.L, nd.H, M, N, p1, p2);
-            BandArgs g1{}, g2{};
-            if (sv.order == BAKRON_ORDER_LA_FIRST) {
-                g1 = BandArgs{b.LAp, b.Ebuf, b.Tbuf, np, np, mp, 0, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
-                g2 = BandArgs{b.LBp, b.Tbuf, b.Wp, mp, mp, np, 1, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
-            } else {
-                g1 = BandArgs{b.LBp, b.Ebuf, b.Tbuf, mp, mp, np, 2, nd.K, nd.L, nd.H, M, N, p1.rlo, 0};
-                g2 = BandArgs{b.Tbuf, b.LAp, b.Wp, np, np, np, 3, nd.K, nd.L, nd.H, M, N, p2.rlo, 1};
-            }
-            g1.rows = p1.rows;
-            g2.rows = p2.rows;
-            if (p1.rows > 0) {
-                hipLaunchKernelGGL(band_gemm_kernel, dim3(p1.cols, (p1.rows + 7) & ~7), dim3(256), 0,
-                                   stream, g1);
-                BK_LAUNCH_CHECK("band_gemm_kernel");
-            }
-            if (p2.rows > 0) {
-                hipLaunchKernelGGL(band_gemm_kernel, dim3(p2.cols, (p2.rows + 7) & ~7), dim3(256), 0,
-                                   stream, g2);
-                BK_LAUNCH_CHECK("band_gemm_kernel");
-            }
-            BK_MARK(2);
+            continue;
         }
+        int *ctr = op.side ? b.ctr + side_k++ : nullptr;
+        int mode, olo, cols, rlo, rows;
+        if (!band_geometry(op, sv.order, M, N, mode, olo, cols, rlo, rows)) continue;
+        float *T = b.Tbuf + (int64_t)nd.depth * mp * np;
+        BandArgs g{};
+        switch (mode) {
+        case 0: g = BandArgs{b.LAp, b.Ebuf, T, np, np, mp, 0, nd.K, nd.L, nd.H, M, N, rlo, 0, rows, olo, cols}; break;
+        case 1: g = BandArgs{b.LBp, T, b.Wp, mp, mp, np, 1, nd.K, nd.L, nd.H, M, N, rlo, 1, rows, olo, cols}; break;
+        case 2: g = BandArgs{b.LBp, b.Ebuf, T, mp, mp, np, 2, nd.K, nd.L, nd.H, M, N, rlo, 0, rows, olo, cols}; break;
+        default: g = BandArgs{T, b.LAp, b.Wp, np, np, np, 3, nd.K, nd.L, nd.H, M, N, rlo, 1, rows, olo, cols}; break;
+        }
+        if (op.side) {
+            // one workgroup per CU, up to one per tile
+            const int wgs = std::min(SIDE_WG, cols * rows);
+            hipLaunchKernelGGL(band_side_kernel, dim3(wgs), dim3(SIDE_THREADS), 0, side ? side : stream, g,
+                               ctr, sv.dev_status);
+            BK_LAUNCH_CHECK("band_side_kernel");
+        } else {
+            hipLaunchKernelGGL(band_gemm_kernel, dim3(cols, (rows + 7) & ~7), dim3(256), 0, stream, g);
+            BK_LAUNCH_CHECK("band_gemm_kernel");
+        }
+        BK_MARK(op.side ? 4 : 2);
     }
     if (sv.sum_e2) {
         hipLaunchKernelGGL(sumsq_partial_kernel, dim3(NPART), dim3(256), 0, stream, b.Ebuf,
@@ -1217,7 +1521,30 @@ constexpr size_t kGraphCache = 16;
 std::mutex g_graph_mu;
 std::map<GraphKey, GraphEntry> g_graphs;
 uint64_t g_graph_clock = 0;
-std::map<int, hipStream_t> g_capture_streams;
+
+// Per device: the streams a graph is captured on, the side stream of eager
+// solves, and the plan's fork / join events (one set for captures, one for
+// eager solves; each set is used under its own lock).
+struct DevStreams {
+    hipStream_t cap = nullptr, cap_side = nullptr, side = nullptr;
+    std::vector<hipEvent_t> cap_ev, ev;
+};
+std::map<int, DevStreams> g_dev;
+std::mutex g_eager_mu;
+
+int32_t grow_events(std::vector<hipEvent_t> &v, int n) {
+    while ((int)v.size() < n) {
+        hipEvent_t e;
+        BK_HIP_CHECK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        v.push_back(e);
+    }
+    return BAKRON_OK;
+}
+
+int32_t make_stream(hipStream_t *s) {
+    if (!*s) BK_HIP_CHECK(hipStreamCreateWithFlags(s, hipStreamNonBlocking));
+    return BAKRON_OK;
+}
 
 // Finds or builds the graph for `sv`; returns it through `exec`.
 int32_t graph_for(const Solve &sv, int dev, const void *ws, hipGraphExec_t *exec) {
@@ -1231,16 +1558,14 @@ int32_t graph_for(const Solve &sv, int dev, const void *ws, hipGraphExec_t *exec
         *exec = it->second.exec;
         return BAKRON_OK;
     }
-    hipStream_t cs;
-    auto cit = g_capture_streams.find(dev);
-    if (cit == g_capture_streams.end()) {
-        BK_HIP_CHECK(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
-        g_capture_streams[dev] = cs;
-    } else {
-        cs = cit->second;
-    }
+    DevStreams &ds = g_dev[dev];
+    int32_t st = make_stream(&ds.cap);
+    if (st == BAKRON_OK) st = make_stream(&ds.cap_side);
+    if (st == BAKRON_OK) st = grow_events(ds.cap_ev, shape_info(sv.M, sv.N).plan.events);
+    if (st != BAKRON_OK) return st;
+    hipStream_t cs = ds.cap;
     BK_HIP_CHECK(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
-    int32_t st = enqueue_solve(sv, cs, nullptr, nullptr);
+    st = enqueue_solve(sv, cs, ds.cap_side, &ds.cap_ev, nullptr, nullptr);
     hipGraph_t graph = nullptr;
     hipError_t ce = hipStreamEndCapture(cs, &graph);
     if (st != BAKRON_OK) {
@@ -1317,21 +1642,22 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     if (flags & BAKRON_FLAG_PHASE_TIMING) {
         std::vector<hipEvent_t> evs;
         std::vector<int> ev_phase;
-        st = enqueue_solve(sv, stream, &evs, &ev_phase);
+        st = enqueue_solve(sv, stream, nullptr, nullptr, &evs, &ev_phase);
         if (st == BAKRON_OK) {
             hipError_t e = hipEventSynchronize(evs.back());
             if (e != hipSuccess) {
                 set_error("hipEventSynchronize: %s", hipGetErrorString(e));
                 st = BAKRON_ERR_HIP;
             } else {
-                for (int k = 0; k < 6; ++k) g_phase_ms[k] = 0.0;
+                for (int k = 0; k < 8; ++k) g_phase_ms[k] = 0.0;
                 for (size_t k = 1; k < evs.size(); ++k) {
                     float ms = 0.0f;
                     (void)hipEventElapsedTime(&ms, evs[k - 1], evs[k]);
                     const int ph = ev_phase[k];
-                    g_phase_ms[ph] += ms;
+                    g_phase_ms[ph == 4 ? 6 : ph] += ms;
                     if (ph == 1) g_phase_ms[4] += 1;
-                    if (ph == 2) g_phase_ms[5] += 2;
+                    if (ph == 2) g_phase_ms[5] += 1;
+                    if (ph == 4) g_phase_ms[7] += 1;
                 }
                 g_phase_valid = true;
             }
@@ -1339,9 +1665,20 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
         for (hipEvent_t e : evs) (void)hipEventDestroy(e);
         return st;
     }
-    if (flags & BAKRON_FLAG_NO_GRAPH) return enqueue_solve(sv, stream, nullptr, nullptr);
     int dev = 0;
     BK_HIP_CHECK(hipGetDevice(&dev));
+    if (flags & BAKRON_FLAG_NO_GRAPH) {
+        std::lock_guard<std::mutex> lock(g_eager_mu);
+        DevStreams *ds;
+        {
+            std::lock_guard<std::mutex> glock(g_graph_mu);
+            ds = &g_dev[dev];
+        }
+        st = make_stream(&ds->side);
+        if (st == BAKRON_OK) st = grow_events(ds->ev, si.plan.events);
+        if (st != BAKRON_OK) return st;
+        return enqueue_solve(sv, stream, ds->side, &ds->ev, nullptr, nullptr);
+    }
     hipGraphExec_t exec;
     st = graph_for(sv, dev, ws, &exec);
     if (st != BAKRON_OK) return st;
