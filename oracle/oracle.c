@@ -96,6 +96,78 @@ int orc_qparams(const float *W, int64_t m, int64_t n, int kind, int bits,
 }
 
 /* ------------------------------------------------------------------ */
+/* per-row scale shrink chosen by an MSE search (review page, free     */
+/* parameters: the per-row scaling factor is shrunk by up to a factor  */
+/* of 2, chosen by an MSE search).  Reading: the candidates are the    */
+/* grid's range (max|w| for symmetric, [min w, max w] for asymmetric)  */
+/* multiplied by p_k = (grid - k) / grid, k = 0 .. maxk (grid 100,     */
+/* maxk 50: p from 1 down to 1/2); each candidate's parameters follow  */
+/* the plain rule on the shrunk range; its error is the sum over the   */
+/* row of (w - v)^2, v the base quantizer's value of w on that grid    */
+/* (clamped); the first candidate with the least error wins (ties keep */
+/* the larger p).  fp32 semantics for the parameters and for v, fp64   */
+/* for the squared errors and their sum (plain order j = 0 .. n-1).    */
+/* k = 0 gives orc_qparams' parameters.                                */
+/* kbest (m) and errs (m x (maxk+1)) may be NULL.                      */
+/* ------------------------------------------------------------------ */
+static float f32(double x) { return (float)x; }
+
+int orc_qparams_mse(const float *W, int64_t m, int64_t n, int kind, int bits, int grid,
+                    int maxk, float *scales, float *zeros, int32_t *kbest, double *errs)
+{
+    if (m < 0 || n < 1 || grid < 1 || maxk < 0 || maxk >= grid) return 1;
+    if (kind != ORC_SYM && kind != ORC_ASYM) return 2;
+    const double qmin = kind == ORC_SYM ? -(double)(1 << (bits - 1)) : 0.0;
+    const double qmax = kind == ORC_SYM ? (double)((1 << (bits - 1)) - 1) : (double)((1 << bits) - 1);
+    for (int64_t i = 0; i < m; i++) {
+        const float *row = W + i * n;
+        float amax = 0.0f, lo = INFINITY, hi = -INFINITY;
+        for (int64_t j = 0; j < n; j++) {
+            if (fabsf(row[j]) > amax) amax = fabsf(row[j]);
+            if (row[j] < lo) lo = row[j];
+            if (row[j] > hi) hi = row[j];
+        }
+        double best = INFINITY;
+        for (int k = 0; k <= maxk; k++) {
+            const float p = f32((double)(grid - k) / (double)grid);
+            float s, z = 0.0f;
+            if (kind == ORC_SYM) {
+                s = f32((double)f32((double)amax * p) / qmax);
+                if (s == 0.0f) s = 1.0f;
+            } else {
+                const float lo_p = f32((double)lo * p), hi_p = f32((double)hi * p);
+                s = f32((double)f32((double)hi_p - lo_p) / qmax);
+                if (s == 0.0f) {
+                    s = 1.0f;
+                } else {
+                    double zz = rint((double)f32(-(double)lo_p / s));
+                    if (zz < 0.0) zz = 0.0;
+                    if (zz > qmax) zz = qmax;
+                    z = (float)zz;
+                }
+            }
+            double err = 0.0;
+            for (int64_t j = 0; j < n; j++) {
+                double c = rint((double)f32((double)row[j] / s)) + z;
+                if (c < qmin) c = qmin;
+                if (c > qmax) c = qmax;
+                const float v = f32((double)s * (c - z));
+                const double d = (double)row[j] - (double)v;
+                err += d * d;
+            }
+            if (errs) errs[i * (maxk + 1) + k] = err;
+            if (err < best) {
+                best = err;
+                scales[i] = s;
+                zeros[i] = z;
+                if (kbest) kbest[i] = k;
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* one rounding decision, with optional adoption of a reference code   */
 /* ------------------------------------------------------------------ */
 typedef struct {

@@ -284,3 +284,61 @@ def test_checkers_detect_planted_mistakes():
     c2[5, 5] += 1 if c2[5, 5] < 7 else -1
     assert oracle.rounding_consistency(c2, r["V"], r["E"], np.diag(LA), np.diag(LB),
                                        s, z, SYM, 4)[0] >= 1
+
+
+# --------------------------------------------------------------------------
+# per-row scale shrink by MSE search (review page, free parameters: shrink up
+# to a factor 2, MSE search); pins independent of the search itself
+# --------------------------------------------------------------------------
+def test_mse_shrink_closed_form_sym():
+    # one entry 1.0 and 63 entries 0.1, INT4 symmetric (qmax 7): on the grid of
+    # p (scale p/7) every 0.1 rounds to code 1 and 1.0 clamps to code 7, so the
+    # error is f(p) = 63 (p/7 - 0.1)^2 + (1 - p)^2, minimal at p = 0.8313; the
+    # grid's best candidate is p = 0.83 (k = 17)
+    W = np.array([[1.0] + [0.1] * 63], np.float32)
+    s, z, kb, errs = oracle.qparams_mse(W, oracle.SYM, 4)
+    assert kb[0] == 17 and z[0] == 0
+    assert s[0] == np.float32(np.float32(0.83) / np.float32(7))
+    for k in range(51):
+        p = (100 - k) / 100
+        f = 63 * (p / 7 - 0.1) ** 2 + (1 - p) ** 2
+        assert abs(errs[0, k] - f) < 1e-6, k
+    assert errs[0, 17] < errs[0, 16] - 1e-4 and errs[0, 17] < errs[0, 18] - 1e-4
+
+
+def test_mse_shrink_closed_form_asym_boundary():
+    # entries 0.0, 1.0 and 63 x 0.1, INT2 asymmetric (qmax 3, zero point 0):
+    # for p > 0.6 the 0.1s round to code 0 (error 63 * 0.01 + (1 - p)^2), for
+    # p < 0.6 to code 1 (error 63 (p/3 - 0.1)^2 + (1 - p)^2, decreasing down to
+    # p = 0.3875): the search ends at its last candidate p = 1/2 with error 0.53
+    W = np.array([[0.0, 1.0] + [0.1] * 63], np.float32)
+    s, z, kb, errs = oracle.qparams_mse(W, oracle.ASYM, 2)
+    assert kb[0] == 50 and z[0] == 0
+    assert abs(errs[0, 50] - (63 * (0.5 / 3 - 0.1) ** 2 + 0.25)) < 1e-6
+    for k in range(0, 40):       # p > 0.6
+        p = (100 - k) / 100
+        assert abs(errs[0, k] - (0.63 + (1 - p) ** 2)) < 1e-6, k
+
+
+def test_mse_shrink_properties():
+    g = np.random.default_rng(11)
+    W = (g.standard_t(4, size=(40, 300)) * 0.02).astype(np.float32)
+    W[3] = 0.0                                   # all candidates tie: keep p = 1
+    for kind, bits in [(oracle.SYM, 4), (oracle.SYM, 3), (oracle.ASYM, 4), (oracle.ASYM, 2)]:
+        s, z, kb, errs = oracle.qparams_mse(W, kind, bits)
+        s0, z0 = oracle.qparams(W, kind, bits)
+        # never worse than the plain grid, and the first minimum is taken
+        assert np.all(errs[np.arange(40), kb] <= errs[:, 0])
+        for i in range(40):
+            assert kb[i] == int(np.argmin(errs[i]))
+        # candidate 0 is the plain quantizer
+        plain = kb == 0
+        assert np.array_equal(s[plain], s0[plain]) and np.array_equal(z[plain], z0[plain])
+        assert kb[3] == 0 and s[3] == 1.0
+        # heavy tails make shrinking pay on most rows
+        assert np.mean(kb > 0) > 0.5
+        # exact under scaling by a power of two
+        s2, z2, kb2, _ = oracle.qparams_mse(W * np.float32(8), kind, bits)
+        nz = np.arange(40) != 3                  # the zero row keeps scale 1
+        assert np.array_equal(kb2, kb) and np.array_equal(z2, z)
+        assert np.array_equal(s2[nz], s[nz] * np.float32(8))
