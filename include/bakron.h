@@ -78,6 +78,15 @@ extern "C" {
                                       returns.  See bakron_last_phase_ms(). */
 #define BAKRON_FLAG_NO_GRAPH 8     /* launch kernel by kernel instead of replaying
                                       the cached executable graph of the solve */
+#define BAKRON_FLAG_MSE_SCALE 16   /* per-row scale shrink by MSE search (review
+                                      page, free parameters: up to a factor 2).
+                                      The row's range is scaled by p = 1, 0.99,
+                                      ..., 0.50; each candidate takes the plain
+                                      parameters of the shrunk range; the first p
+                                      with the least sum over the row of
+                                      (w - v)^2 (v the clamped base-quantizer value
+                                      of w, fp32; sum in fp64) wins.  Symmetric and
+                                      asymmetric kinds; ignored for BAKRON_Q_UNIT. */
 
 /*
  * bakron_hessian -- Kronecker factor from samples, with damping.

@@ -76,7 +76,7 @@ def _load():
         D = ctypes.c_double
         lib.orc_qparams.argtypes = [P, I64, I64, I, I, P, P]
         lib.orc_qparams.restype = I
-        lib.orc_qparams_mse.argtypes = [P, I64, I64, I, I, I, I, P, P, P, P]
+        lib.orc_qparams_mse.argtypes = [P, I64, I64, I, I, I, I, P, P, P, P, P, P]
         lib.orc_qparams_mse.restype = I
         lib.orc_naive.argtypes = [I64, I64, P, P, P, P, P, I, I, I, I, P, D, P, P, P, P, P]
         lib.orc_naive.restype = I
@@ -122,22 +122,27 @@ def qparams(W: np.ndarray, kind: int, bits: int):
 MSE_GRID, MSE_MAXK = 100, 50
 
 
-def qparams_mse(W: np.ndarray, kind: int, bits: int, grid: int = MSE_GRID, maxk: int = MSE_MAXK):
+def qparams_mse(W: np.ndarray, kind: int, bits: int, grid: int = MSE_GRID, maxk: int = MSE_MAXK,
+                cands: bool = False):
     """Per-row parameters with the scale shrink chosen by an MSE search (review
     page, free parameters: shrink up to a factor 2, MSE search).  Candidates
     p_k = (grid - k) / grid, k = 0..maxk, applied to the row's range; the
     first candidate with the least sum of squared errors (w - v)^2 wins.
-    Returns (scales, zeros, kbest, errs) with errs[i, k] each candidate's error."""
+    Returns (scales, zeros, kbest, errs); with cands=True also (cand_s, cand_z):
+    errs, cand_s, cand_z[i, k] are candidate k's error, scale and zero point."""
     W = np.ascontiguousarray(W, dtype=np.float32)
     m, n = W.shape
     s = np.empty(m, np.float32)
     z = np.empty(m, np.float32)
     kb = np.empty(m, np.int32)
     errs = np.empty((m, maxk + 1), np.float64)
-    rc = _load().orc_qparams_mse(_p(W), m, n, kind, bits, grid, maxk, _p(s), _p(z), _p(kb), _p(errs))
+    cs = np.empty((m, maxk + 1), np.float32)
+    cz = np.empty((m, maxk + 1), np.float32)
+    rc = _load().orc_qparams_mse(_p(W), m, n, kind, bits, grid, maxk, _p(s), _p(z), _p(kb), _p(errs),
+                                 _p(cs), _p(cz))
     if rc:
         raise ValueError(f"orc_qparams_mse rc={rc}")
-    return s, z, kb, errs
+    return (s, z, kb, errs, cs, cz) if cands else (s, z, kb, errs)
 
 
 def _prep(W, LA, LB, scales, zeros):

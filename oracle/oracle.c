@@ -108,12 +108,14 @@ int orc_qparams(const float *W, int64_t m, int64_t n, int kind, int bits,
 /* the larger p).  fp32 semantics for the parameters and for v, fp64   */
 /* for the squared errors and their sum (plain order j = 0 .. n-1).    */
 /* k = 0 gives orc_qparams' parameters.                                */
-/* kbest (m) and errs (m x (maxk+1)) may be NULL.                      */
+/* kbest (m), errs, cand_s and cand_z (m x (maxk+1): every candidate's */
+/* error, scale and zero point) may be NULL.                           */
 /* ------------------------------------------------------------------ */
 static float f32(double x) { return (float)x; }
 
 int orc_qparams_mse(const float *W, int64_t m, int64_t n, int kind, int bits, int grid,
-                    int maxk, float *scales, float *zeros, int32_t *kbest, double *errs)
+                    int maxk, float *scales, float *zeros, int32_t *kbest, double *errs,
+                    float *cand_s, float *cand_z)
 {
     if (m < 0 || n < 1 || grid < 1 || maxk < 0 || maxk >= grid) return 1;
     if (kind != ORC_SYM && kind != ORC_ASYM) return 2;
@@ -156,6 +158,8 @@ int orc_qparams_mse(const float *W, int64_t m, int64_t n, int kind, int bits, in
                 err += d * d;
             }
             if (errs) errs[i * (maxk + 1) + k] = err;
+            if (cand_s) cand_s[i * (maxk + 1) + k] = s;
+            if (cand_z) cand_z[i * (maxk + 1) + k] = z;
             if (err < best) {
                 best = err;
                 scales[i] = s;

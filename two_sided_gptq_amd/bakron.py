@@ -19,6 +19,7 @@ Q_SYM, Q_ASYM, Q_UNIT = 0, 1, 2
 ORDER_AUTO, ORDER_LA_FIRST, ORDER_LB_FIRST = 0, 1, 2
 FLAG_PHASE_TIMING = 4
 FLAG_NO_GRAPH = 8
+FLAG_MSE_SCALE = 16
 DEV_NONFINITE, DEV_NOT_PD = 1, 2
 
 EXPORTS = (
@@ -130,7 +131,7 @@ def quantize_workspace_size(m: int, n: int, kind: int, bits: int) -> int:
 
 def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_E=False,
              want_sum=False, dev_status=None, timing=False, graph=True, workspace=None, out=None,
-             stream=None):
+             stream=None, mse=False):
     """Run bakron_quantize.  Returns a dict with codes (int8), scales, zeros
     (None unless asymmetric), V, E, sum_e2 (device tensors or None)."""
     lib = load()
@@ -150,7 +151,8 @@ def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_
         )
     if workspace is None:
         workspace = _workspace(quantize_workspace_size(m, n, kind, bits), dev)
-    flags = int(order) | (FLAG_PHASE_TIMING if timing else 0) | (0 if graph else FLAG_NO_GRAPH)
+    flags = (int(order) | (FLAG_PHASE_TIMING if timing else 0) | (0 if graph else FLAG_NO_GRAPH) |
+             (FLAG_MSE_SCALE if mse else 0))
     rc = lib.bakron_quantize(_ptr(W), m, n, _ptr(LA), _ptr(LB), kind, bits, _ptr(out["codes"]),
                              _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["V"]),
                              _ptr(out["E"]), _ptr(out["sum_e2"]), _ptr(dev_status), flags,

@@ -40,12 +40,78 @@ constexpr int NPART = 1024;  // partial sums of the e^2 reduction
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------------ qparams
+// Per-row scale shrink by MSE search (review page, free parameters: the
+// per-row scale shrinks by up to a factor 2, chosen by an MSE search).  The
+// candidates scale the row's range (max |w|, or min w and max w) by
+// p_k = (MSE_GRID - k) / MSE_GRID, k = 0 .. MSE_MAXK, and take the plain
+// parameters of the shrunk range; a candidate's error is the row's sum of
+// (w - v)^2, v the base quantizer's clamped value of w on that grid; the first
+// candidate with the least error wins.  Parameters and v in fp32 (no fused
+// operations), squared errors summed in fp64: per thread over j = t (mod 256),
+// then a fixed butterfly in each wave and the four waves in order.  k = 0 is
+// the plain quantizer.  All 256 threads call it; returns (s, z) to all.
+constexpr int MSE_GRID = 100, MSE_MAXK = 50;
+
+__device__ void mse_search(const float *row, int64_t n, int kind, int bits, float amax, float lo,
+                           float hi, float &s_out, float &z_out) {
+#pragma clang fp contract(off)
+    __shared__ double red[4];
+    __shared__ float best_s, best_z;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const float qmin = kind == BAKRON_Q_SYM ? -(float)(1 << (bits - 1)) : 0.0f;
+    const float qmax = kind == BAKRON_Q_SYM ? (float)((1 << (bits - 1)) - 1) : (float)((1 << bits) - 1);
+    double best = INFINITY;  // meaningful in thread 0
+    for (int k = 0; k <= MSE_MAXK; ++k) {
+        const float p = (float)(MSE_GRID - k) / (float)MSE_GRID;
+        float s, z = 0.0f;
+        if (kind == BAKRON_Q_SYM) {
+            const float a = amax * p;
+            s = a / qmax;
+            if (s == 0.0f) s = 1.0f;
+        } else {
+            const float lo_p = lo * p, hi_p = hi * p;
+            const float range = hi_p - lo_p;
+            s = range / qmax;
+            if (s == 0.0f) s = 1.0f;
+            else z = fminf(fmaxf(rintf(-lo_p / s), 0.0f), qmax);
+        }
+        double acc = 0.0;
+        for (int64_t j = t; j < n; j += 256) {
+            const float x = row[j];
+            const float c = fminf(fmaxf(rintf(x / s) + z, qmin), qmax);
+            const float v = s * (c - z);
+            const double d = (double)x - (double)v;
+            const double d2 = d * d;
+            acc = acc + d2;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double o = __shfl_xor(acc, off);
+            acc = acc + o;
+        }
+        if (lane == 0) red[w] = acc;
+        __syncthreads();
+        if (t == 0) {
+            const double err = ((red[0] + red[1]) + red[2]) + red[3];
+            if (err < best) {
+                best = err;
+                best_s = s;
+                best_z = z;
+            }
+        }
+        __syncthreads();
+    }
+    s_out = best_s;
+    z_out = best_z;
+}
+
 // One workgroup per padded row.  Rows >= m get s = 1, z = 0 (the padding is
-// all zeros, so every padded entry rounds to its zero point exactly).
+// all zeros, so every padded entry rounds to its zero point exactly).  With
+// mse (symmetric and asymmetric kinds) the scale shrink comes from mse_search.
 __global__ __launch_bounds__(256) void qparams_kernel(
     const float *__restrict__ W, int64_t m, int64_t n, int kind, int bits,
     float *__restrict__ scales, float *__restrict__ zeros, float *__restrict__ sc_pad,
-    float *__restrict__ zp_pad, int32_t *dev_status) {
+    float *__restrict__ zp_pad, int32_t *dev_status, int mse) {
     __shared__ float s_amax[256], s_lo[256], s_hi[256];
     __shared__ int s_bad[256];
     const int64_t i = blockIdx.x;
@@ -89,6 +155,8 @@ __global__ __launch_bounds__(256) void qparams_kernel(
                 z = fminf(fmaxf(rintf(-s_lo[0] / s), 0.0f), qmax);
             }
         }
+        if (mse && kind != BAKRON_Q_UNIT && !s_bad[0])
+            mse_search(row, n, kind, bits, s_amax[0], s_lo[0], s_hi[0], s, z);
         if (t == 0) {
             scales[i] = s;
             if (zeros) zeros[i] = z;
@@ -1381,6 +1449,7 @@ struct Solve {
     const float *W, *LA, *LB;
     int64_t m, n, mp, np;
     int M, N, order, qkind, qbits, qmin, qmax;
+    int mse;  // per-row scale shrink by MSE search
     int8_t *codes;
     float *scales, *zeros, *V, *E;
     double *sum_e2;
@@ -1415,7 +1484,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     const int64_t m = sv.m, n = sv.n, mp = sv.mp, np = sv.np;
     BK_MARK(-1);
     hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, sv.W, m, n,
-                       sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status);
+                       sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status, sv.mse);
     BK_LAUNCH_CHECK("qparams_kernel");
     const unsigned rl_blocks = 256u * 8u;
     const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.W) & 15) == 0);
@@ -1496,7 +1565,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
 // buffers' current contents.  At most kGraphCache entries; the least recently
 // used one is dropped.
 struct GraphKey {
-    int dev, order, qkind, qbits;
+    int dev, order, qkind, qbits, mse;
     int64_t m, n;
     const void *p[12];
     bool operator<(const GraphKey &o) const {
@@ -1504,6 +1573,7 @@ struct GraphKey {
         if (order != o.order) return order < o.order;
         if (qkind != o.qkind) return qkind < o.qkind;
         if (qbits != o.qbits) return qbits < o.qbits;
+        if (mse != o.mse) return mse < o.mse;
         if (m != o.m) return m < o.m;
         if (n != o.n) return n < o.n;
         for (int k = 0; k < 12; ++k)
@@ -1548,7 +1618,7 @@ int32_t make_stream(hipStream_t *s) {
 
 // Finds or builds the graph for `sv`; returns it through `exec`.
 int32_t graph_for(const Solve &sv, int dev, const void *ws, hipGraphExec_t *exec) {
-    GraphKey key{dev, sv.order, sv.qkind, sv.qbits, sv.m, sv.n,
+    GraphKey key{dev, sv.order, sv.qkind, sv.qbits, sv.mse, sv.m, sv.n,
                  {sv.W, sv.LA, sv.LB, sv.codes, sv.scales, sv.zeros, sv.V, sv.E, sv.sum_e2,
                   sv.dev_status, ws, nullptr}};
     std::lock_guard<std::mutex> lock(g_graph_mu);
@@ -1608,7 +1678,8 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     BK_REQUIRE(m >= 1 && n >= 1 && m <= MAX_DIM && n <= MAX_DIM, "bad shape %lld x %lld",
                (long long)m, (long long)n);
     BK_REQUIRE(valid_quantizer(qkind, qbits), "unsupported quantizer kind=%d bits=%d", qkind, qbits);
-    BK_REQUIRE((flags & ~(BAKRON_ORDER_MASK | BAKRON_FLAG_PHASE_TIMING | BAKRON_FLAG_NO_GRAPH)) == 0 &&
+    BK_REQUIRE((flags & ~(BAKRON_ORDER_MASK | BAKRON_FLAG_PHASE_TIMING | BAKRON_FLAG_NO_GRAPH |
+                          BAKRON_FLAG_MSE_SCALE)) == 0 &&
                    (flags & BAKRON_ORDER_MASK) != 3,
                "unknown flags 0x%x", flags);
     const size_t need = bakron_quantize_workspace_size(m, n, qkind, qbits);
@@ -1632,6 +1703,7 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     if (sv.order == BAKRON_ORDER_AUTO) sv.order = si.auto_order;
     sv.qkind = qkind;
     sv.qbits = qbits;
+    sv.mse = (flags & BAKRON_FLAG_MSE_SCALE) && qkind != BAKRON_Q_UNIT;
     if (qkind == BAKRON_Q_SYM) { sv.qmin = -(1 << (qbits - 1)); sv.qmax = (1 << (qbits - 1)) - 1; }
     else if (qkind == BAKRON_Q_ASYM) { sv.qmin = 0; sv.qmax = (1 << qbits) - 1; }
     else { sv.qmin = -128; sv.qmax = 127; }
