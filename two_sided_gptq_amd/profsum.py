@@ -37,28 +37,39 @@ def short_name(n: str) -> str:
     return m.group(1) if m else n[:48]
 
 
-def _window(rows):
-    """Dispatches of the last timed solve: between the last two parameter kernels."""
+def _windows(rows):
+    """The last timed graph solve (between the last two parameter kernels) and
+    the timing pass after it (from the last parameter kernel on), where the
+    benchmark runs the same plan in order on one stream and takes its phase
+    times and per-launch averages."""
     rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
     q = [i for i, r in enumerate(rows) if "qparams_kernel" in r["Kernel_Name"]]
-    return rows[q[-2]:q[-1]] if len(q) >= 2 else rows
+    if len(q) < 2:
+        return rows, rows
+    return rows[q[-2]:q[-1]], rows[q[-1]:]
 
 
-def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> str:
-    out = []
-    rows = list(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_trace.csv"))))
-    win = _window(rows)
+def _table(out, win, title):
     per = collections.defaultdict(list)
     for r in win:
         per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    span = int(win[-1]["End_Timestamp"]) - int(win[0]["Start_Timestamp"])
-    out.append(f"Kernel trace command: `{command}`\n")
-    out.append(f"### One solve (last timed bakron_quantize call): {span / 1e3:.1f} us over {len(win)} dispatches\n")
+    span = max(int(r["End_Timestamp"]) for r in win) - int(win[0]["Start_Timestamp"])
+    out.append(f"### {title}: {span / 1e3:.1f} us over {len(win)} dispatches\n")
     out.append("| kernel | launches | total us | avg us | min us | max us |")
     out.append("|---|---|---|---|---|---|")
     for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"| {k} | {len(v)} | {sum(v) / 1e3:.1f} | {statistics.mean(v) / 1e3:.2f} | "
                    f"{min(v) / 1e3:.2f} | {max(v) / 1e3:.2f} |")
+    out.append("")
+
+
+def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> str:
+    out = []
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_trace.csv"))))
+    graph_win, timing_win = _windows(rows)
+    out.append(f"Kernel trace command: `{command}`\n")
+    _table(out, graph_win, "One timed solve (graph replay; deferred products overlap the leaves)")
+    _table(out, timing_win, "Timing pass (the same plan in order on one stream; bench.py's per-launch averages)")
     out.append("\n### rocprofv3 --stats (whole command)\n")
     out.append("| kernel | calls | average ns | % |")
     out.append("|---|---|---|---|")
@@ -91,7 +102,7 @@ def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> s
         out.append(f"| {k} | {len(d['FETCH_SIZE'])} | {f:.1f} | {w:.1f} | {b:.4g} |")
     out.append("\nMachine-readable (read by bench.py):\n")
     out.append(f"    source_sha256_16: {source_hash()}")
-    for k in ("band_gemm_kernel", "leaf_kernel<false>"):
+    for k in ("band_gemm_kernel", "band_side_kernel", "leaf_kernel<false>"):
         if k in traffic:
             out.append(f"    traffic_bytes_per_dispatch: {k} {traffic[k]:.6g}")
     return "\n".join(out) + "\n"
