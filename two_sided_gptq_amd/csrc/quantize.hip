@@ -223,12 +223,6 @@ struct LeafArgs {
     float *Cd, *Cr;   // contributions of the previous tile diagonal: from the tile above / to the left
 };
 
-// sum over the 4 consecutive lanes of a group (all 4 end with the total)
-__device__ inline float group4_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    return x;
-}
 
 __device__ inline float dot4(const float4 a, const float4 b, float s) {
     s = fmaf(a.x, b.x, s);
