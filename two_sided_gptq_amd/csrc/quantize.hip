@@ -283,10 +283,13 @@ __shared__ __align__(16) float lf_E[TB * LP];
 __shared__ __align__(16) float lf_Z[TB * LP];    // lf_Z[c][k] = Z[k][c]
 __shared__ __align__(16) float lf_B[TB * LP];    // LB[I,I]
 __shared__ __align__(16) float lf_A[TB * LP];    // LA[J,J]
-__shared__ float4 lf_Ab[NCX * 2];                // CX + c: LA[c][c], LA[c][c-1 .. c-7]; 0 off 0..63
-__shared__ float lf_ila[NCX];                    // CX + c: 1 / LA_cc; 0 off 0..63
+// The chain's per-step tables carry a larger alignment so that they are laid out
+// before the big arrays, below 64 KB, where a load's constant part fits the
+// instruction's offset field.
+__shared__ __align__(32) float4 lf_Ab[NCX * 2];  // CX + c: LA[c][c], LA[c][c-1 .. c-7]; 0 off 0..63
+__shared__ __align__(32) float lf_ila[NCX];      // CX + c: 1 / LA_cc; 0 off 0..63
 __shared__ float4 lf_row[TB];                    // (s, 1/s, z, 1/LB_rr)
-__shared__ __align__(16) float lf_bulk[2 * 2 * TB * LJ];  // [buffer][direction][row][step in block]
+__shared__ __align__(32) float lf_bulk[2 * 2 * TB * LJ];  // [buffer][direction][row][step in block]
 __shared__ float lf_sink[3 * TB];                // write targets of idle lanes
 __shared__ __align__(16) float lf_P[2 * TB * GP]; // push operands: LA(J+1,J), then LB(I+1,I)
 
