@@ -352,15 +352,14 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
         const int d = LJ * t + p;
         const float la[8] = {cb.a[p][0].x, cb.a[p][0].y, cb.a[p][0].z, cb.a[p][0].w,
                              cb.a[p][1].x, cb.a[p][1].y, cb.a[p][1].z, cb.a[p][1].w};
-        // recent terms j = 2 .. LJ + p (steps s0 .. d-2), then the fresh j = 1
-        float y = 0.0f, s2 = 0.0f;
+        // the bulk, then the recent terms j = LJ + p .. 2 (steps s0 .. d-2),
+        // then the fresh j = 1
+        float y = bulk1[p], s2 = bulk2[p];
 #pragma unroll
         for (int j = LJ + p; j >= 2; --j) {
             y = fmaf(st.eh[j - 1], la[j], y);
             s2 = fmaf(st.lbb[j], st.zl[j - 1], s2);
         }
-        y += bulk1[p];
-        s2 += bulk2[p];
         y = fmaf(st.eh[0], la[1], y);
         s2 = fmaf(st.lbb[1], st.zl[0], s2);
         const float P = wv[p] - fmaf(st.lbb[0], y, s2);
