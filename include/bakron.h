@@ -198,12 +198,17 @@ int32_t bakron_schedule_plan(int64_t m, int64_t n, int32_t flags, int32_t *ops, 
                              int64_t *count);
 
 /* Per-phase times (ms) of the calling thread's last bakron_quantize call made
- * with BAKRON_FLAG_PHASE_TIMING (the plan run in order on one stream): out[0]
- * quantizer parameters + relayout, out[1] leaf kernels, out[2] band GEMM
- * kernels on the critical stream, out[3] finalise, out[4] leaf launches,
- * out[5] critical band GEMM launches, out[6] deferred band kernels, out[7]
- * deferred band launches.  Returns BAKRON_ERR_INVALID_ARG if no such call was
- * made. */
+ * with BAKRON_FLAG_PHASE_TIMING.  That call runs the plan in order on one
+ * stream with an event after every step: out[0] quantizer parameters +
+ * relayout, out[1] leaf kernels, out[2] band GEMM kernels on the critical
+ * stream, out[3] finalise, out[4] leaf launches, out[5] critical band GEMM
+ * launches, out[6] deferred band kernels, out[7] deferred band launches.
+ * These intervals include each launch's dispatch latency.  The call then
+ * replays the critical band launches alone, and then the deferred ones alone,
+ * each as a one-off graph whose kernels start back to back, timed by events
+ * around the graph launch: out[8] and out[9] (kernel time without dispatch
+ * gaps; the replays rewrite the workspace, not the outputs).  Returns
+ * BAKRON_ERR_INVALID_ARG if no such call was made. */
 int32_t bakron_last_phase_ms(double *out);
 
 const char *bakron_status_string(int32_t status);

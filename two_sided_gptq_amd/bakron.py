@@ -191,7 +191,7 @@ def schedule_plan(m: int, n: int, order: int = ORDER_AUTO) -> list:
 
 
 PHASE_KEYS = ("prep_ms", "leaf_ms", "band_ms", "final_ms", "leaf_launches", "band_launches",
-              "side_ms", "side_launches")
+              "side_ms", "side_launches", "band_replay_ms", "side_replay_ms")
 
 
 def last_phase_ms() -> dict:

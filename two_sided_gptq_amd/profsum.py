@@ -38,15 +38,18 @@ def short_name(n: str) -> str:
 
 
 def _windows(rows):
-    """The last timed graph solve (between the last two parameter kernels) and
-    the timing pass after it (from the last parameter kernel on), where the
-    benchmark runs the same plan in order on one stream and takes its phase
-    times and per-launch averages."""
+    """The last timed graph solve (between the last two parameter kernels), the
+    timing pass after it (the same plan in order on one stream, from the last
+    parameter kernel to its final reduction), and the band replays that follow
+    (the critical band launches alone, then the deferred ones), from which the
+    benchmark takes the band kernels' average launch durations."""
     rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
     q = [i for i, r in enumerate(rows) if "qparams_kernel" in r["Kernel_Name"]]
     if len(q) < 2:
-        return rows, rows
-    return rows[q[-2]:q[-1]], rows[q[-1]:]
+        return rows, rows, []
+    end = next((i for i in range(q[-1], len(rows)) if "sumsq_final_kernel" in rows[i]["Kernel_Name"]),
+               len(rows) - 1)
+    return rows[q[-2]:q[-1]], rows[q[-1]:end + 1], rows[end + 1:]
 
 
 def _table(out, win, title):
@@ -66,10 +69,12 @@ def _table(out, win, title):
 def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> str:
     out = []
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_trace.csv"))))
-    graph_win, timing_win = _windows(rows)
+    graph_win, timing_win, replay_win = _windows(rows)
     out.append(f"Kernel trace command: `{command}`\n")
     _table(out, graph_win, "One timed solve (graph replay; deferred products overlap the leaves)")
-    _table(out, timing_win, "Timing pass (the same plan in order on one stream; bench.py's per-launch averages)")
+    _table(out, timing_win, "Timing pass (the same plan in order on one stream, an event after every step)")
+    if replay_win:
+        _table(out, replay_win, "Band replays (critical, then deferred launches alone; bench.py's band averages)")
     out.append("\n### rocprofv3 --stats (whole command)\n")
     out.append("| kernel | calls | average ns | % |")
     out.append("|---|---|---|---|")
