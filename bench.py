@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=896,
                    help="edge of the leading block timed with the CPU oracle (0 = skip)")
     p.add_argument("--order", type=int, default=0)
+    p.add_argument("--antidiag", action="store_true",
+                   help="also time BaKron-antidiagonal once on the same inputs and report the ratio")
     p.add_argument("--eager", action="store_true",
                    help="launch kernel by kernel instead of replaying the solve's graph")
     p.add_argument("--copy-probe", action="store_true",
@@ -198,6 +200,16 @@ def main():
                  "achieved_GBs": leaf_gbs, "hbm_frac": leaf_gbs / HBM_PEAK_GBS},
         "schedule": sched,
     }
+    if args.antidiag:
+        # the pages' comparison (review page, "If this is right": BaKron about 27x
+        # faster than BaKron-antidiagonal at 4096 x 4096): one antidiagonal solve
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        bakron.quantize_antidiag(W, LA, LB, kind=w.qkind, bits=w.qbits, dev_status=status)
+        torch.cuda.synchronize()
+        ad_ms = (time.perf_counter() - t0) * 1e3
+        result["antidiag"] = {"ms": ad_ms, "ratio_vs_bakron": ad_ms / ms, "pages_ratio": 27}
+        print(f"[bench] BaKron-antidiagonal: {ad_ms:.1f} ms ({ad_ms / ms:.0f}x)", file=sys.stderr, flush=True)
     if args.cpu_sample > 0:
         LA_h = LA.cpu().numpy()
         LB_h = LB.cpu().numpy()

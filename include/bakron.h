@@ -154,6 +154,23 @@ int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
                         int32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * bakron_quantize_antidiag -- BaKron-antidiagonal, the pages' comparison
+ * variant (review page "If this is right": BaKron runs about 27x faster than
+ * it at 4096 x 4096; "Core claim", Theorem 3.2: both give the same output).
+ * Every entry anti-diagonal d = i + j is rounded at once, then its rank-|d|
+ * update W[i'][j'] -= sum_{(i,j) on d} LB[i'][i] e_ij LA[j'][j] is applied to
+ * the rest of the matrix: O(m + n) steps, O(m^2 n^2) work.  Arguments,
+ * quantizer and outputs as for bakron_quantize (no sum_e2; no flags); two
+ * kernel launches per anti-diagonal on `stream`, no graph.  Its own workspace
+ * (bakron_quantize_antidiag_workspace_size).  Returns as bakron_quantize.
+ */
+size_t bakron_quantize_antidiag_workspace_size(int64_t m, int64_t n, int32_t qkind, int32_t qbits);
+int32_t bakron_quantize_antidiag(const float *W, int64_t m, int64_t n, const float *LA,
+                                 const float *LB, int32_t qkind, int32_t qbits, int8_t *codes,
+                                 float *scales, float *zeros, float *V, float *E,
+                                 int32_t *dev_status, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * bakron_schedule_info -- the static schedule for an m x n solve, without
  * touching the GPU.  out[0..14]:
  *   0 tile size b           1 leaf launches (tile anti-diagonals M+N-1)

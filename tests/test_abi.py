@@ -77,6 +77,11 @@ def test_argument_errors_without_device(lib):
     rc = lib.bakron_quantize(fake, 4, 4, fake, fake, 0, 4, fake, fake, None, None, None, None, None,
                              0, P(4096 + 8), 1 << 30, None)
     assert rc == 2  # misaligned workspace
+    assert lib.bakron_quantize_antidiag(None, 4, 4, fake, fake, 0, 4, fake, fake, None, None, None,
+                                        None, fake, 1 << 20, None) == 1
+    assert lib.bakron_quantize_antidiag(fake, 4, 4, fake, fake, 0, 4, fake, fake, None, None, None,
+                                        None, fake, 8, None) == 2
+    assert lib.bakron_quantize_antidiag_workspace_size(4, 4, 0, 5) == 0
     assert lib.bakron_hessian(None, 4, 4, 0.01, fake, None, 0, None) == 1
     assert lib.bakron_hessian(fake, 4, 4, -1.0, fake, None, 0, None) == 1
     assert lib.bakron_factor(fake, 0, fake, None, fake, 1 << 20, None) == 1

@@ -26,6 +26,7 @@ EXPORTS = (
     "bakron_hessian_workspace_size", "bakron_hessian",
     "bakron_factor_workspace_size", "bakron_factor",
     "bakron_quantize_workspace_size", "bakron_quantize",
+    "bakron_quantize_antidiag_workspace_size", "bakron_quantize_antidiag",
     "bakron_schedule_info", "bakron_schedule_plan", "bakron_last_phase_ms",
     "bakron_status_string", "bakron_last_error",
 )
@@ -59,6 +60,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bakron_quantize_workspace_size.restype = SZ
     lib.bakron_quantize.argtypes = [P, I64, I64, P, P, I32, I32, P, P, P, P, P, P, P, I32, P, SZ, P]
     lib.bakron_quantize.restype = I32
+    lib.bakron_quantize_antidiag_workspace_size.argtypes = [I64, I64, I32, I32]
+    lib.bakron_quantize_antidiag_workspace_size.restype = SZ
+    lib.bakron_quantize_antidiag.argtypes = [P, I64, I64, P, P, I32, I32, P, P, P, P, P, P, P, SZ, P]
+    lib.bakron_quantize_antidiag.restype = I32
     lib.bakron_schedule_info.argtypes = [I64, I64, I32, ctypes.POINTER(D)]
     lib.bakron_schedule_info.restype = I32
     lib.bakron_schedule_plan.argtypes = [I64, I64, I32, ctypes.POINTER(I32), I64,
@@ -158,6 +163,33 @@ def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_
                              _ptr(out["E"]), _ptr(out["sum_e2"]), _ptr(dev_status), flags,
                              _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "bakron_quantize")
+    return out
+
+
+def quantize_antidiag(W, LA, LB, kind=Q_SYM, bits=4, want_V=True, want_E=False, dev_status=None,
+                      stream=None):
+    """Run bakron_quantize_antidiag (BaKron-antidiagonal).  Returns a dict with
+    codes, scales, zeros (None unless asymmetric), V, E (device tensors or None)."""
+    lib = load()
+    W = _f32_dev(W, "W")
+    LA = _f32_dev(LA, "LA")
+    LB = _f32_dev(LB, "LB")
+    m, n = W.shape
+    dev = W.device
+    out = dict(
+        codes=torch.empty((m, n), dtype=torch.int8, device=dev),
+        scales=torch.empty(m, dtype=torch.float32, device=dev),
+        zeros=torch.empty(m, dtype=torch.float32, device=dev) if kind == Q_ASYM else None,
+        V=torch.empty((m, n), dtype=torch.float32, device=dev) if want_V else None,
+        E=torch.empty((m, n), dtype=torch.float32, device=dev) if want_E else None,
+    )
+    size = int(lib.bakron_quantize_antidiag_workspace_size(m, n, kind, bits))
+    workspace = _workspace(size, dev)
+    rc = lib.bakron_quantize_antidiag(_ptr(W), m, n, _ptr(LA), _ptr(LB), kind, bits, _ptr(out["codes"]),
+                                      _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["V"]),
+                                      _ptr(out["E"]), _ptr(dev_status), _ptr(workspace),
+                                      workspace.numel(), _stream(stream))
+    _check(rc, "bakron_quantize_antidiag")
     return out
 
 

@@ -1014,6 +1014,104 @@ __global__ __launch_bounds__(256) void sumsq_final_kernel(const double *partial,
     if (threadIdx.x == 0) *out = red[0];
 }
 
+// ------------------------------------------------------- BaKron-antidiagonal
+// The comparison variant of the pages (pith.science review of arXiv
+// 2608.06291, "If this is right": BaKron runs about 27x faster than it at
+// 4096 x 4096; "Core claim": all variants give the same output).  Every entry
+// anti-diagonal d is rounded at once, then its rank-|d| update is applied to
+// the rest of the matrix:
+//   W[i'][j'] -= sum over the entries (i, j) of d of LB[i'][i] e_ij LA[j'][j].
+// The per-entry rounding is the leaf's, operation for operation.
+
+// Rounds the entries (i, d - i), i = i_min .. i_min + cnt - 1; e to eb[i - i_min].
+template <bool ZP>
+__global__ __launch_bounds__(256) void ad_round_kernel(
+    const float *__restrict__ Wp, const float *__restrict__ LAp, const float *__restrict__ LBp,
+    const float *__restrict__ sc, const float *__restrict__ zp, int64_t mp, int64_t np, int64_t n,
+    int d, int i_min, int cnt, float qminf, float qmaxf, int8_t *__restrict__ codes,
+    float *__restrict__ V, float *__restrict__ E, float *__restrict__ eb, int32_t *dev_status) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= cnt) return;
+    const int64_t i = i_min + k, j = d - i;
+    const float P = Wp[i * np + j];
+    const float s = sc[i], rs = 1.0f / s, z = zp[i];
+    float qz, res;
+    if (ZP) {
+        qz = __builtin_amdgcn_fmed3f(rintf(P * rs) + z, qminf, qmaxf);
+        res = fmaf(-s, qz - z, P);
+    } else {
+        qz = __builtin_amdgcn_fmed3f(rintf(P * rs), qminf, qmaxf);
+        res = fmaf(-s, qz, P);
+    }
+    const float e = res * ((1.0f / LBp[i * mp + i]) * (1.0f / LAp[j * np + j]));
+    eb[k] = e;
+    codes[i * n + j] = (int8_t)(int)qz;
+    if (V) V[i * n + j] = s * (qz - z);
+    if (E) E[i * n + j] = e;
+    if (!isfinite(e) && dev_status) atomicOr(dev_status, BAKRON_DEV_NONFINITE);
+}
+
+// The rank-cnt update of diagonal d on the 64 x 64 output tiles of W from tile
+// row i_min / 64 and tile column (d - i_min - cnt + 1) / 64 on (rows above the
+// diagonal's first row and columns left of its first column get exact zeros:
+// LB and LA are lower triangular), skipping tiles that lie on or before d.
+// C[i'][j'] -= sum_k A[i'][k] B[j'][k], A[i'][k] = LB[i'][i_min + k],
+// B[j'][k] = e_k LA[j'][d - i_min - k], k in chunks of 64 (zero past cnt);
+// fp32 MFMA as in band_gemm_kernel.
+__global__ __launch_bounds__(256) void ad_update_kernel(
+    float *__restrict__ Wp, const float *__restrict__ LAp, const float *__restrict__ LBp,
+    const float *__restrict__ eb, int64_t mp, int64_t np, int d, int i_min, int cnt, int ti0,
+    int tj0) {
+    const int ti = ti0 + blockIdx.y, tj = tj0 + blockIdx.x;
+    if (TB * (ti + tj) + 2 * (TB - 1) <= d) return;  // every entry of the tile is at or before d
+    __shared__ __align__(16) float As[TB * GP];
+    __shared__ __align__(16) float Bs[TB * GP];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wr = w >> 1, wc = w & 1;
+    const int lr = tid >> 4, lc = (tid & 15) * 4;
+    floatx16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    const float *ap = As + (wr * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
+    const float *bp = Bs + (wc * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
+    for (int kc = 0; kc < cnt; kc += TB) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = lr + 16 * q;
+            const int64_t gi = (int64_t)ti * TB + r, gj = (int64_t)tj * TB + r;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = kc + lc + t;
+                float a = 0.0f, b = 0.0f;
+                if (k < cnt) {
+                    a = LBp[gi * mp + i_min + k];
+                    b = eb[k] * LAp[gj * np + (d - i_min - k)];
+                }
+                As[r * GP + lc + t] = a;
+                Bs[r * GP + lc + t] = b;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s4 = 0; s4 < 8; ++s4) {
+            const float4 av = *reinterpret_cast<const float4 *>(ap + 4 * s4);
+            const float4 bv = *reinterpret_cast<const float4 *>(bp + 4 * s4);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
+        }
+    }
+    const int col = lane & 31;
+    float *cb = Wp + (int64_t)(ti * TB + wr * 32 + 4 * (lane >> 5)) * np + (int64_t)tj * TB + wc * 32 + col;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        float *c = cb + (int64_t)(8 * (v >> 2) + (v & 3)) * np;
+        *c = *c - acc[v];
+    }
+}
+
 // ---------------------------------------------------------------- schedule
 struct Node {
     int leaf;  // 1: leaf(K); 0: band(K, L, H)
@@ -1833,5 +1931,88 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     st = graph_for(sv, dev, ws, &exec);
     if (st != BAKRON_OK) return st;
     BK_HIP_CHECK(hipGraphLaunch(exec, stream));
+    return BAKRON_OK;
+}
+
+// --------------------------------------------------------------------------
+// BaKron-antidiagonal: one entry anti-diagonal at a time (comparison variant).
+namespace bakron {
+namespace {
+size_t carve_antidiag(void *ws, int64_t m, int64_t n, float **Wp, float **LAp, float **LBp,
+                      float **sc, float **zp, float **eb) {
+    const int64_t mp = round_up(m, TB), np = round_up(n, TB);
+    Carver cv(ws);
+    float *w_ = cv.take<float>(mp * np);
+    float *la = cv.take<float>(np * np);
+    float *lb = cv.take<float>(mp * mp);
+    float *s_ = cv.take<float>(mp);
+    float *z_ = cv.take<float>(mp);
+    float *e_ = cv.take<float>(std::min(m, n));
+    if (Wp) { *Wp = w_; *LAp = la; *LBp = lb; *sc = s_; *zp = z_; *eb = e_; }
+    return cv.used;
+}
+}  // namespace
+}  // namespace bakron
+
+extern "C" size_t bakron_quantize_antidiag_workspace_size(int64_t m, int64_t n, int32_t qkind,
+                                                          int32_t qbits) {
+    if (m < 1 || n < 1 || m > MAX_DIM || n > MAX_DIM || !valid_quantizer(qkind, qbits)) return 0;
+    return carve_antidiag(reinterpret_cast<void *>(256), m, n, nullptr, nullptr, nullptr, nullptr,
+                          nullptr, nullptr);
+}
+
+extern "C" int32_t bakron_quantize_antidiag(const float *W, int64_t m, int64_t n, const float *LA,
+                                            const float *LB, int32_t qkind, int32_t qbits,
+                                            int8_t *codes, float *scales, float *zeros, float *V,
+                                            float *E, int32_t *dev_status, void *ws,
+                                            size_t ws_bytes, void *stream_) {
+    clear_error();
+    BK_REQUIRE(W && LA && LB && codes && scales, "W, LA, LB, codes and scales must be non-NULL");
+    BK_REQUIRE(m >= 1 && n >= 1 && m <= MAX_DIM && n <= MAX_DIM, "bad shape %lld x %lld",
+               (long long)m, (long long)n);
+    BK_REQUIRE(valid_quantizer(qkind, qbits), "unsupported quantizer kind=%d bits=%d", qkind, qbits);
+    const size_t need = bakron_quantize_antidiag_workspace_size(m, n, qkind, qbits);
+    if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
+        set_error("workspace needs %zu bytes at 256-byte alignment (got %zu at %p)", need,
+                  ws_bytes, ws);
+        return BAKRON_ERR_WORKSPACE;
+    }
+    int32_t st = check_device();
+    if (st != BAKRON_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int64_t mp = round_up(m, TB), np = round_up(n, TB);
+    const int M = (int)(mp / TB), N = (int)(np / TB);
+    float *Wp, *LAp, *LBp, *sc, *zp, *eb;
+    carve_antidiag(ws, m, n, &Wp, &LAp, &LBp, &sc, &zp, &eb);
+    int qmin, qmax;
+    if (qkind == BAKRON_Q_SYM) { qmin = -(1 << (qbits - 1)); qmax = (1 << (qbits - 1)) - 1; }
+    else if (qkind == BAKRON_Q_ASYM) { qmin = 0; qmax = (1 << qbits) - 1; }
+    else { qmin = -128; qmax = 127; }
+    hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, W, m, n, qkind, qbits,
+                       scales, zeros, sc, zp, dev_status, 0);
+    BK_LAUNCH_CHECK("qparams_kernel");
+    const unsigned rl_blocks = 256u * 8u;
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, W, m, n, Wp, mp, np, 0, 0);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LA, n, n, LAp, np, np, 1, 0);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LB, m, m, LBp, mp, mp, 1, 0);
+    BK_LAUNCH_CHECK("relayout_kernel");
+    for (int d = 0; d <= (int)(m + n - 2); ++d) {
+        const int i_min = (int)std::max<int64_t>(0, d - n + 1), i_max = (int)std::min<int64_t>(m - 1, d);
+        const int cnt = i_max - i_min + 1;
+        if (qkind == BAKRON_Q_ASYM)
+            hipLaunchKernelGGL(ad_round_kernel<true>, dim3((cnt + 255) / 256), dim3(256), 0, stream, Wp, LAp,
+                               LBp, sc, zp, mp, np, n, d, i_min, cnt, (float)qmin, (float)qmax, codes, V, E,
+                               eb, dev_status);
+        else
+            hipLaunchKernelGGL(ad_round_kernel<false>, dim3((cnt + 255) / 256), dim3(256), 0, stream, Wp, LAp,
+                               LBp, sc, zp, mp, np, n, d, i_min, cnt, (float)qmin, (float)qmax, codes, V, E,
+                               eb, dev_status);
+        BK_LAUNCH_CHECK("ad_round_kernel");
+        if (d == (int)(m + n - 2)) break;
+        const int ti0 = i_min / TB, tj0 = (d - i_max) / TB;
+        hipLaunchKernelGGL(ad_update_kernel, dim3(N - tj0, M - ti0), dim3(256), 0, stream, Wp, LAp, LBp, eb,
+                           mp, np, d, i_min, cnt, ti0, tj0);
+        BK_LAUNCH_CHECK("ad_update_kernel");
+    }
     return BAKRON_OK;
 }
