@@ -1174,7 +1174,7 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
 // leaves in diagonal order and, for every band node, the products that feed
 // its first target diagonals.  A node whose right part spans R = L - H >=
 // SIDE_MIN_R diagonals keeps only the targets K + H .. a - 1, a = K + H +
-// (R >> SIDE_SHIFT), critical: its first product over the T diagonals from a
+// (R >> shift), critical: its first product over the T diagonals from a
 // on and its second product over the targets from a on go to the side stream.
 // They are forked by events once their inputs exist (the sources are final
 // when the node starts; the second product also reads the critical part of T)
@@ -1186,7 +1186,14 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
 // gives the same results bit for bit.
 constexpr int OP_LEAF = 0, OP_BAND = 1, OP_RECORD = 2, OP_WAIT = 3;
 constexpr int SIDE_MIN_R = 16;
-constexpr int SIDE_SHIFT = 2;
+// The deferred work should fit beside the leaves: the side kernel sustains
+// about 48 TFLOP/s on its CUs and a leaf launch lasts about 25 us, so about
+// 1.2e9 flops per leaf launch.  A shape keeps a quarter of each wide node's
+// targets critical (shift 2) if that defers no more than this, else half
+// (shift 1).  Measured: 4096 x 4096 defers 0.77e9 per leaf with shift 2 and
+// runs faster than with shift 1; 11008 x 4096 and 4096 x 14336 defer 2.1e9
+// and 3.0e9 with shift 2 and run 5 % and 9 % faster with shift 1.
+constexpr double SIDE_BUDGET = 1.2e9;
 
 struct Op {
     int kind;
@@ -1202,7 +1209,7 @@ struct Plan {
     int events = 0;
 };
 
-Plan build_plan(int M, int N) {
+Plan build_plan(int M, int N, int shift) {
     Plan pl;
     std::vector<Node> nodes;
     build_nodes(0, M + N - 1, nodes);
@@ -1231,7 +1238,7 @@ Plan build_plan(int M, int N) {
             continue;
         }
         const int R = nd.L - nd.H, end = nd.K + nd.L;
-        const int keep = R >= SIDE_MIN_R ? (R >> SIDE_SHIFT) : R;
+        const int keep = R >= SIDE_MIN_R ? (R >> shift) : R;
         if (keep < R) {
             const int a = nd.K + nd.H + keep;
             const int e1 = pl.events++, e3 = pl.events++;
@@ -1404,11 +1411,14 @@ const ShapeInfo &shape_info(int M, int N) {
     auto it = g_shapes.find(key);
     if (it != g_shapes.end()) return it->second;
     ShapeInfo s{};
-    s.plan = build_plan(M, N);
-    s.band[1] = band_flops(s.plan, BAKRON_ORDER_LA_FIRST, M, N);
-    s.band[2] = band_flops(s.plan, BAKRON_ORDER_LB_FIRST, M, N);
+    for (int shift = 2; shift >= 1; --shift) {
+        s.plan = build_plan(M, N, shift);
+        s.band[1] = band_flops(s.plan, BAKRON_ORDER_LA_FIRST, M, N);
+        s.band[2] = band_flops(s.plan, BAKRON_ORDER_LB_FIRST, M, N);
+        s.auto_order = s.band[2].exec < s.band[1].exec ? BAKRON_ORDER_LB_FIRST : BAKRON_ORDER_LA_FIRST;
+        if (s.band[s.auto_order].side_useful <= SIDE_BUDGET * (M + N - 1)) break;
+    }
     pull_counts(M, N, &s.pull_flops, &s.pull_leaves);
-    s.auto_order = s.band[2].exec < s.band[1].exec ? BAKRON_ORDER_LB_FIRST : BAKRON_ORDER_LA_FIRST;
     s.side_ops = 0;
     for (const Op &op : s.plan.ops) s.side_ops += op.kind == OP_BAND && op.side;
     return g_shapes.emplace(key, s).first->second;
