@@ -802,6 +802,16 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
         rb3 = *reinterpret_cast<const float4 *>(b_ + 3 * sb);                        \
     } while (0)
     BK_GLOAD(klo);
+    // accumulator layout of the 32 x 32 MFMA: lane l holds column l % 32;
+    // register v holds row 8 (v / 4) + 4 (l / 32) + v % 4.  The old values of
+    // a subtracted tile are loaded now, so their latency overlaps the K loop.
+    float *cb = g.C + (int64_t)(ci * TB + wr * 32 + 4 * (lane >> 5)) * g.ldc + (int64_t)cj * TB +
+                wc * 32 + (lane & 31);
+    float old[16];
+    if (g.subtract) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) old[v] = cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc];
+    }
     floatx16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -832,16 +842,7 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
         }
     }
 #undef BK_GLOAD
-    // accumulator layout of the 32 x 32 MFMA: lane l holds column l % 32;
-    // register v holds row 8 (v / 4) + 4 (l / 32) + v % 4.
-    const int col = lane & 31;
-    float *cb = g.C + (int64_t)(ci * TB + wr * 32 + 4 * (lane >> 5)) * g.ldc + (int64_t)cj * TB +
-                wc * 32 + col;
     if (g.subtract) {
-        // all 16 old values in flight at once, then the stores
-        float old[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) old[v] = cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc];
 #pragma unroll
         for (int v = 0; v < 16; ++v) cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc] = old[v] - acc[v];
     } else {
