@@ -51,54 +51,139 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float *__restr
     }
 }
 
+// 1 / sqrt(x) for x > 0: the hardware estimate and two Newton steps, within
+// about an ulp of the rounded quotient.
+__device__ __forceinline__ double rsqrt_nr(double x) {
+    double y = __builtin_amdgcn_rsq(x);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const double h = 0.5 * x * y;
+        y = fma(y, fma(-h, y, 0.5), y);
+    }
+    return y;
+}
+
 // One 64 x 64 diagonal block at (off, off): its Cholesky factor and the
-// inverse of that factor, in LDS, right-looking and interleaved.  At column j:
-//   phase 1  c_jj = sqrt(A_jj); column j below the diagonal / c_jj; row j of
-//            X = C^-1 from its completed pending sums: X_jj = 1 / c_jj,
-//            X_jc = -S_jc / c_jj (c < j)
-//   phase 2  trailing update A_ik -= C_ij C_kj (j < k <= i) and pending sums
-//            S_ic += C_ij X_jc (i > j, c <= j)
-// with a barrier after each phase.  Thread (i, q) = (t / 4, t % 4) takes the
-// entries of row i with column = q (mod 4).  Writes the block of C (upper
-// part zero) and of X.
+// inverse of that factor, right-looking and interleaved, one workgroup.
+// Thread (i, q) = (t / 4, t % 4) owns the entries of row i in the columns
+// k = q (mod 4), 16 of A (the trailing matrix, then C) and 16 of S (pending
+// sums of X = C^-1).  Columns go in groups jb of four; during group jb the
+// thread holds, in registers with fixed indices,
+//   ar[m'] = A[i][4 (jb + m') + q]   (m' = 0..15; zero past the block)
+//   sr[m'] = S[i][4 (jb - m') + q]   (m' = 0..15; zero before the block)
+// and between groups both windows move by one (the finished A entry ar[0]
+// goes to the LDS staging copy of the block).  At column j = 4 jb + qj:
+//   publish  r = 1 / sqrt(A_jj) (from the diagonal's owner), the column
+//            A[k][j] unscaled (from its owners, rows k > j), and the pending
+//            row S[j][c] with -1 at c = j (from row j's threads)
+//   barrier
+//   update   the column's owners scale C_ij = A_ij r; every row i > j, with
+//            w = A_ij r^2: A_ik -= w A_kj (k > j), i.e. C_ij C_kj, and
+//            S_ic -= w S'_jc (c <= j), i.e. + C_ij X_jc with X_jc = -S_jc r
+//            (c < j), X_jj = r; row j's threads keep r_j.
+// Row j of X is X_jc = -S_jc r_j (c < j), X_jj = r_j, formed when the block is
+// written out.  Rows i <= j take w = 0, which leaves them unchanged.  The
+// published rows sit in LDS rows of 32 with zero padding on the side the
+// windows run past, so only the entries of the current group need a mask.
+// Two LDS sets alternate by column parity, so one barrier per column
+// separates every write from the reads of the same set.  The block is staged
+// through LDS on the way in and out, so the global accesses are coalesced.
 __global__ __launch_bounds__(256) void base_kernel(const double *__restrict__ G, double *C, double *X,
                                                    int64_t dp, int64_t off, int32_t *dev_status) {
-    __shared__ double A[FT * FP];
-    __shared__ double S[FT * FP];  // pending sums of X, then X
-    __shared__ int s_bad;
+    constexpr int NM = FT / 4;
+    __shared__ double st[FT * FP];          // staging of the block
+    // rows of 34 doubles, so the four rows a wave reads start 16 bytes apart in the banks
+    constexpr int RW = 2 * NM + 2;
+    __shared__ double s_col[2][4][RW];  // [parity][k % 4][k / 4], zero at k / 4 >= 16
+    __shared__ double s_xs[2][4][RW];   // [parity][c % 4][16 + c / 4], zero below 16
+    __shared__ double s_rc[2];
     const int t = threadIdx.x, ri = t >> 2, q = t & 3;
     for (int idx = t; idx < FT * FT; idx += 256) {
         const int i = idx >> 6, k = idx & 63;
-        A[i * FP + k] = k <= i ? G[(off + i) * dp + off + k] : 0.0;
-        S[i * FP + k] = 0.0;
+        st[i * FP + k] = k <= i ? G[(off + i) * dp + off + k] : 0.0;
     }
-    if (t == 0) s_bad = 0;
+    for (int idx = t; idx < 2 * 4 * RW; idx += 256) {
+        (&s_col[0][0][0])[idx] = 0.0;
+        (&s_xs[0][0][0])[idx] = 0.0;
+    }
     __syncthreads();
-    for (int j = 0; j < FT; ++j) {
-        double ajj = A[j * FP + j];
-        if (!(ajj > 0.0) || !isfinite(ajj)) {
-            if (t == 0) s_bad = 1;
-            ajj = 1.0;
-        }
-        const double cjj = sqrt(ajj), rcjj = 1.0 / cjj;
-        if (t < FT) {
-            if (t > j) A[t * FP + j] *= rcjj;
-            else S[j * FP + t] = (t == j) ? rcjj : -S[j * FP + t] * rcjj;
-        }
-        __syncthreads();
-        if (ri > j) {
-            const double cij = A[ri * FP + j];
-            for (int k = j + 1 + q; k <= ri; k += 4) A[ri * FP + k] -= cij * A[k * FP + j];
-            for (int c = q; c <= j; c += 4) S[ri * FP + c] += cij * S[j * FP + c];
-        }
-        __syncthreads();
+    double ar[NM], sr[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        ar[m] = st[ri * FP + 4 * m + q];
+        sr[m] = 0.0;
     }
+    int bad = 0;
+    double rrow = 0.0;  // r_i of this thread's row, once column i is done
+    for (int jb = 0; jb < NM; ++jb) {
+        if (jb > 0) {
+            st[ri * FP + 4 * (jb - 1) + q] = ar[0];
+#pragma unroll
+            for (int m = 0; m + 1 < NM; ++m) ar[m] = ar[m + 1];
+            ar[NM - 1] = 0.0;
+#pragma unroll
+            for (int m = NM - 1; m > 0; --m) sr[m] = sr[m - 1];
+            sr[0] = 0.0;
+        }
+#pragma unroll
+        for (int qj = 0; qj < 4; ++qj) {
+            const int j = 4 * jb + qj, par = qj & 1;
+            // publish
+            if (ri == j && q == qj) {
+                double ajj = ar[0];
+                if (!(ajj > 0.0) || !isfinite(ajj)) {
+                    bad = 1;
+                    ajj = 1.0;
+                }
+                s_rc[par] = rsqrt_nr(ajj);
+            }
+            if (q == qj && ri > j) s_col[par][ri & 3][ri >> 2] = ar[0];
+            if (ri == j) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+                    s_xs[par][q][NM + jb - m] = (m == 0 && q == qj) ? -1.0 : sr[m];
+            }
+            __syncthreads();
+            // update
+            const double rc = s_rc[par];
+            rrow = ri == j ? rc : rrow;
+            const double w = ri > j ? s_col[par][ri & 3][ri >> 2] * rc * rc : 0.0;
+            const double *cq = &s_col[par][q][jb];
+            const double *xq = &s_xs[par][q][NM + jb];
+            {   // the current group: column 4 jb + q is past j for q > qj, j itself for q = qj
+                const double v = fma(-w, cq[0], ar[0]);
+                const double sc = ri > j ? ar[0] * rc : ar[0];
+                ar[0] = q > qj ? v : (q == qj ? sc : ar[0]);
+                const double u = fma(-w, xq[0], sr[0]);
+                sr[0] = q <= qj ? u : sr[0];
+            }
+#pragma unroll
+            for (int m = 1; m < NM; ++m) {
+                ar[m] = fma(-w, cq[m], ar[m]);
+                sr[m] = fma(-w, xq[-m], sr[m]);
+            }
+        }
+    }
+    // C (upper part zero, diagonal sqrt of the last A_ii) and X through LDS
+    st[ri * FP + 4 * (NM - 1) + q] = ar[0];
+    __syncthreads();
     for (int idx = t; idx < FT * FT; idx += 256) {
         const int i = idx >> 6, k = idx & 63;
-        C[(off + i) * dp + off + k] = k < i ? A[i * FP + k] : (k == i ? sqrt(A[i * FP + i]) : 0.0);
-        X[(off + i) * dp + off + k] = k <= i ? S[i * FP + k] : 0.0;
+        const double v = st[i * FP + k];
+        C[(off + i) * dp + off + k] = k < i ? v : (k == i ? sqrt(v) : 0.0);
     }
-    if (t == 0 && s_bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const int k = 4 * (NM - 1 - m) + q;
+        st[ri * FP + k] = k < ri ? -sr[m] * rrow : (k == ri ? rrow : 0.0);
+    }
+    __syncthreads();
+    for (int idx = t; idx < FT * FT; idx += 256) {
+        const int i = idx >> 6, k = idx & 63;
+        X[(off + i) * dp + off + k] = st[i * FP + k];
+    }
+    if (bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
 }
 
 // C (M x N) = beta C + alpha sum_k A[i][k] op(B)[k][j], op(B)[k][j] = B[j][k]
