@@ -221,6 +221,7 @@ struct LeafArgs {
     int64_t m, n;
     int32_t *dev_status;
     float *Cd, *Cr;   // contributions of the previous tile diagonal: from the tile above / to the left
+    int out_vec;      // n % 4 == 0, codes 4-byte and V, E 16-byte aligned: outputs in groups of 4
 };
 
 
@@ -693,17 +694,42 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     }
     // caller-visible outputs
     int bad = 0;
-    for (int idx = tid; idx < TB * TB; idx += LEAF_THREADS) {
-        const int r = idx >> 6, c = idx & 63;
-        const int64_t gi = r0 + r, gj = c0 + c;
-        bad |= !isfinite(Es[r * LP + c]);
-        if (gi < a.m && gj < a.n) {
-            const float qf = lf_Wk[r * WSP + r + c];
-            const int8_t code = (int8_t)(int)qf;
-            a.codes[gi * a.n + gj] = code;
-            const float4 rc = s_row[r];
-            if (a.V) a.V[gi * a.n + gj] = rc.x * (qf - rc.z);
-            if (a.E) a.E[gi * a.n + gj] = Es[r * LP + c];
+    if (a.out_vec) {
+        // groups of 4 columns: with n % 4 == 0 a group is wholly inside or outside
+        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
+            const int r = idx >> 4, c4 = (idx & 15) * 4;
+            const int64_t gi = r0 + r, gj = c0 + c4;
+            const float4 e = *reinterpret_cast<const float4 *>(Es + r * LP + c4);
+            bad |= !isfinite(e.x) | !isfinite(e.y) | !isfinite(e.z) | !isfinite(e.w);
+            if (gi < a.m && gj < a.n) {
+                const float *wk = lf_Wk + r * WSP + r + c4;
+                const float q0 = wk[0], q1 = wk[1], q2 = wk[2], q3 = wk[3];
+                const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q0) |
+                                        ((uint32_t)(uint8_t)(int8_t)(int)q1 << 8) |
+                                        ((uint32_t)(uint8_t)(int8_t)(int)q2 << 16) |
+                                        ((uint32_t)(uint8_t)(int8_t)(int)q3 << 24);
+                *reinterpret_cast<uint32_t *>(a.codes + gi * a.n + gj) = packed;
+                const float4 rc = s_row[r];
+                if (a.V)
+                    *reinterpret_cast<float4 *>(a.V + gi * a.n + gj) =
+                        make_float4(rc.x * (q0 - rc.z), rc.x * (q1 - rc.z), rc.x * (q2 - rc.z),
+                                    rc.x * (q3 - rc.z));
+                if (a.E) *reinterpret_cast<float4 *>(a.E + gi * a.n + gj) = e;
+            }
+        }
+    } else {
+        for (int idx = tid; idx < TB * TB; idx += LEAF_THREADS) {
+            const int r = idx >> 6, c = idx & 63;
+            const int64_t gi = r0 + r, gj = c0 + c;
+            bad |= !isfinite(Es[r * LP + c]);
+            if (gi < a.m && gj < a.n) {
+                const float qf = lf_Wk[r * WSP + r + c];
+                const int8_t code = (int8_t)(int)qf;
+                a.codes[gi * a.n + gj] = code;
+                const float4 rc = s_row[r];
+                if (a.V) a.V[gi * a.n + gj] = rc.x * (qf - rc.z);
+                if (a.E) a.E[gi * a.n + gj] = Es[r * LP + c];
+            }
         }
     }
     if (bad && a.dev_status) atomicOr(a.dev_status, BAKRON_DEV_NONFINITE);
@@ -1606,8 +1632,12 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     BK_LAUNCH_CHECK("relayout_kernel");
     BK_MARK(0);
 
+    const auto aligned = [](const void *p, uintptr_t to) {
+        return (reinterpret_cast<uintptr_t>(p) & (to - 1)) == 0;
+    };
+    const int out_vec = n % 4 == 0 && aligned(sv.codes, 4) && aligned(sv.V, 16) && aligned(sv.E, 16);
     LeafArgs la{b.Wp, b.Ebuf, b.LAp, b.LBp, b.sc, b.zp, mp, np, M, N, sv.order, sv.qmin, sv.qmax,
-                sv.codes, sv.V, sv.E, m, n, sv.dev_status, b.Cd, b.Cr};
+                sv.codes, sv.V, sv.E, m, n, sv.dev_status, b.Cd, b.Cr, out_vec};
     const Plan &plan = shape_info(M, N).plan;
     hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, stream, b.ctr, b.nctr);
     BK_LAUNCH_CHECK("zero_i32_kernel");
