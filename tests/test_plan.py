@@ -126,10 +126,12 @@ def happens_before(plan):
     return steps, anc
 
 
-def check_plan(m, n, order):
+def check_plan(m, n, order, mutate=None):
     si = bakron.schedule_info(m, n, order)
     order = int(si["order"])
     plan = bakron.schedule_plan(m, n, order)
+    if mutate is not None:
+        plan = mutate(plan)
     M, N = (m + 63) // 64, (n + 63) // 64
     steps, anc = happens_before(plan)
     hb = lambda a, b: (anc[b] >> a) & 1 == 1
@@ -182,7 +184,8 @@ def check_plan(m, n, order):
     assert set(cover) == expect, (m, n)
     # some work is deferred once the recursion is wide enough
     n_side = sum(1 for op in steps if op["kind"] == BAND and op["side"] == 1)
-    assert n_side == si["side_launches"]
+    if mutate is None:
+        assert n_side == si["side_launches"]
     return n_side
 
 
@@ -207,3 +210,22 @@ def test_plan_flops_split(lib):
         si = bakron.schedule_info(m, n)
         assert 0 < si["side_useful_flops"] < si["useful_band_flops"]
         assert si["side_launches"] < si["band_launches"]
+
+
+def _drop(pred):
+    """A plan mutation that removes the first step matching pred."""
+    def mutate(plan):
+        k = next(i for i, op in enumerate(plan) if pred(plan, i))
+        return plan[:k] + plan[k + 1:]
+    return mutate
+
+
+def test_plan_check_catches_missing_sync(lib):
+    # each kind of event edge is needed: the model rejects the plan without the
+    # side stream's wait before a deferred product (its fork), or without the
+    # critical stream's wait for it (its join)
+    fork = _drop(lambda pl, i: pl[i]["kind"] == WAIT and pl[i]["side"] == 1)
+    join = _drop(lambda pl, i: pl[i]["kind"] == WAIT and pl[i]["side"] == 0)
+    for mutate in (fork, join):
+        with pytest.raises(AssertionError):
+            check_plan(4096, 4096, 1, mutate)

@@ -700,7 +700,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
             const int r = idx >> 4, c4 = (idx & 15) * 4;
             const int64_t gi = r0 + r, gj = c0 + c4;
             const float4 e = *reinterpret_cast<const float4 *>(Es + r * LP + c4);
-            bad |= !isfinite(e.x) | !isfinite(e.y) | !isfinite(e.z) | !isfinite(e.w);
+            bad |= (!isfinite(e.x) || !isfinite(e.y) || !isfinite(e.z) || !isfinite(e.w));
             if (gi < a.m && gj < a.n) {
                 const float *wk = lf_Wk + r * WSP + r + c4;
                 const float q0 = wk[0], q1 = wk[1], q2 = wk[2], q3 = wk[3];
