@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--order", type=int, default=0)
     p.add_argument("--antidiag", action="store_true",
                    help="also time BaKron-antidiagonal once on the same inputs and report the ratio")
+    p.add_argument("--split", choices=["cols", "rows", "both"], default=None,
+                   help="also time the hybrid schedule (one top-level column / row split, "
+                        "BAKRON_FLAG_SPLIT_*) on the same inputs and report its time")
     p.add_argument("--eager", action="store_true",
                    help="launch kernel by kernel instead of replaying the solve's graph")
     p.add_argument("--copy-probe", action="store_true",
@@ -210,6 +213,26 @@ def main():
         ad_ms = (time.perf_counter() - t0) * 1e3
         result["antidiag"] = {"ms": ad_ms, "ratio_vs_bakron": ad_ms / ms, "pages_ratio": 27}
         print(f"[bench] BaKron-antidiagonal: {ad_ms:.1f} ms ({ad_ms / ms:.0f}x)", file=sys.stderr, flush=True)
+    if args.split:
+        # the hybrid schedule (review page, "Circularity Check": BaKron-recursive's
+        # split, Appendix C), timed like the main line
+        result["split"] = {}
+        for sp in (["cols", "rows"] if args.split == "both" else [args.split]):
+            def split_step():
+                bakron.quantize(W, LA, LB, kind=w.qkind, bits=w.qbits, order=args.order,
+                                dev_status=status, workspace=ws, out=out, split=sp)
+            for _ in range(args.warmup):
+                split_step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                split_step()
+            torch.cuda.synchronize()
+            sp_ms = (time.perf_counter() - t0) / args.steps * 1e3
+            result["split"][sp] = {"ms_per_step": sp_ms, "ratio_vs_bakron": sp_ms / ms}
+            print(f"[bench] split {sp}: {sp_ms:.3f} ms/step ({sp_ms / ms:.2f}x)", file=sys.stderr, flush=True)
+        if int(status.item()) != 0:
+            raise SystemExit(f"device status {int(status.item())}")
     if args.cpu_sample > 0:
         LA_h = LA.cpu().numpy()
         LB_h = LB.cpu().numpy()

@@ -87,6 +87,15 @@ extern "C" {
                                       (w - v)^2 (v the clamped base-quantizer value
                                       of w, fp32; sum in fp64) wins.  Symmetric and
                                       asymmetric kinds; ignored for BAKRON_Q_UNIT. */
+#define BAKRON_FLAG_SPLIT_COLS 32  /* hybrid schedule (review "Circularity Check":
+                                      BaKron-recursive's recurrence, Appendix C): solve
+                                      the tile columns 0 .. N/2-1, apply their updates to
+                                      the rest (W2 -= LB E1 LA21^T), solve the rest;
+                                      each half by the recursion over anti-diagonals.
+                                      Same result (Theorem 3.2). */
+#define BAKRON_FLAG_SPLIT_ROWS 64  /* the same with the tile rows 0 .. M/2-1 first
+                                      (W2 -= LB21 E1 LA^T).  At most one split flag;
+                                      neither with BAKRON_FLAG_PHASE_TIMING. */
 
 /*
  * bakron_hessian -- Kronecker factor from samples, with damping.

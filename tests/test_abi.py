@@ -69,8 +69,13 @@ def test_argument_errors_without_device(lib):
                              0, fake, 1 << 20, None)
     assert rc == 1
     rc = lib.bakron_quantize(fake, 4, 4, fake, fake, 0, 4, fake, fake, None, None, None, None, None,
-                             0x40, fake, 1 << 20, None)
+                             0x80, fake, 1 << 20, None)
     assert rc == 1
+    # the two split flags exclude each other, and a split is not phase-timed
+    for flags in (0x20 | 0x40, 0x20 | 0x4, 0x40 | 0x4):
+        rc = lib.bakron_quantize(fake, 4, 4, fake, fake, 0, 4, fake, fake, None, None, None, None,
+                                 None, flags, fake, 1 << 20, None)
+        assert rc == 1 and b"SPLIT" in lib.bakron_last_error(), flags
     rc = lib.bakron_quantize(fake, 4, 4, fake, fake, 0, 4, fake, fake, None, None, None, None, None,
                              0, fake, 16, None)
     assert rc == 2 and b"workspace" in lib.bakron_last_error()

@@ -20,6 +20,8 @@ ORDER_AUTO, ORDER_LA_FIRST, ORDER_LB_FIRST = 0, 1, 2
 FLAG_PHASE_TIMING = 4
 FLAG_NO_GRAPH = 8
 FLAG_MSE_SCALE = 16
+FLAG_SPLIT_COLS = 32
+FLAG_SPLIT_ROWS = 64
 DEV_NONFINITE, DEV_NOT_PD = 1, 2
 
 EXPORTS = (
@@ -136,9 +138,10 @@ def quantize_workspace_size(m: int, n: int, kind: int, bits: int) -> int:
 
 def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_E=False,
              want_sum=False, dev_status=None, timing=False, graph=True, workspace=None, out=None,
-             stream=None, mse=False):
+             stream=None, mse=False, split=None):
     """Run bakron_quantize.  Returns a dict with codes (int8), scales, zeros
-    (None unless asymmetric), V, E, sum_e2 (device tensors or None)."""
+    (None unless asymmetric), V, E, sum_e2 (device tensors or None).  split:
+    None, "cols" or "rows" (the hybrid schedule, BAKRON_FLAG_SPLIT_*)."""
     lib = load()
     W = _f32_dev(W, "W")
     LA = _f32_dev(LA, "LA")
@@ -156,8 +159,11 @@ def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_
         )
     if workspace is None:
         workspace = _workspace(quantize_workspace_size(m, n, kind, bits), dev)
+    if split not in (None, "cols", "rows"):
+        raise ValueError(f"split must be None, 'cols' or 'rows', not {split!r}")
     flags = (int(order) | (FLAG_PHASE_TIMING if timing else 0) | (0 if graph else FLAG_NO_GRAPH) |
-             (FLAG_MSE_SCALE if mse else 0))
+             (FLAG_MSE_SCALE if mse else 0) | (FLAG_SPLIT_COLS if split == "cols" else 0) |
+             (FLAG_SPLIT_ROWS if split == "rows" else 0))
     rc = lib.bakron_quantize(_ptr(W), m, n, _ptr(LA), _ptr(LB), kind, bits, _ptr(out["codes"]),
                              _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["V"]),
                              _ptr(out["E"]), _ptr(out["sum_e2"]), _ptr(dev_status), flags,

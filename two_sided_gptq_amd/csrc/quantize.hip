@@ -218,10 +218,11 @@ struct LeafArgs {
     int qmin, qmax;
     int8_t *codes;
     float *V, *E;
-    int64_t m, n;
+    int64_t m, n;     // bounds of the outputs (rows, columns of the solved block)
     int32_t *dev_status;
     float *Cd, *Cr;   // contributions of the previous tile diagonal: from the tile above / to the left
-    int out_vec;      // n % 4 == 0, codes 4-byte and V, E 16-byte aligned: outputs in groups of 4
+    int out_vec;      // ldo % 4 == 0, codes 4-byte and V, E 16-byte aligned: outputs in groups of 4
+    int64_t ldo;      // row stride of codes, V and E
 };
 
 
@@ -695,7 +696,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     // caller-visible outputs
     int bad = 0;
     if (a.out_vec) {
-        // groups of 4 columns: with n % 4 == 0 a group is wholly inside or outside
+        // groups of 4 columns: with ldo % 4 == 0 (and so n % 4 == 0) a group is
+        // wholly inside or outside
         for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
             const int r = idx >> 4, c4 = (idx & 15) * 4;
             const int64_t gi = r0 + r, gj = c0 + c4;
@@ -708,13 +710,13 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
                                         ((uint32_t)(uint8_t)(int8_t)(int)q1 << 8) |
                                         ((uint32_t)(uint8_t)(int8_t)(int)q2 << 16) |
                                         ((uint32_t)(uint8_t)(int8_t)(int)q3 << 24);
-                *reinterpret_cast<uint32_t *>(a.codes + gi * a.n + gj) = packed;
+                *reinterpret_cast<uint32_t *>(a.codes + gi * a.ldo + gj) = packed;
                 const float4 rc = s_row[r];
                 if (a.V)
-                    *reinterpret_cast<float4 *>(a.V + gi * a.n + gj) =
+                    *reinterpret_cast<float4 *>(a.V + gi * a.ldo + gj) =
                         make_float4(rc.x * (q0 - rc.z), rc.x * (q1 - rc.z), rc.x * (q2 - rc.z),
                                     rc.x * (q3 - rc.z));
-                if (a.E) *reinterpret_cast<float4 *>(a.E + gi * a.n + gj) = e;
+                if (a.E) *reinterpret_cast<float4 *>(a.E + gi * a.ldo + gj) = e;
             }
         }
     } else {
@@ -725,10 +727,10 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
             if (gi < a.m && gj < a.n) {
                 const float qf = lf_Wk[r * WSP + r + c];
                 const int8_t code = (int8_t)(int)qf;
-                a.codes[gi * a.n + gj] = code;
+                a.codes[gi * a.ldo + gj] = code;
                 const float4 rc = s_row[r];
-                if (a.V) a.V[gi * a.n + gj] = rc.x * (qf - rc.z);
-                if (a.E) a.E[gi * a.n + gj] = Es[r * LP + c];
+                if (a.V) a.V[gi * a.ldo + gj] = rc.x * (qf - rc.z);
+                if (a.E) a.E[gi * a.ldo + gj] = Es[r * LP + c];
             }
         }
     }
@@ -750,7 +752,11 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
 //   mode 1  (LA first, product 2)  W(I',J') -= sum_I LB(I',I) Tt(J',I)^T
 //   mode 2  (LB first, product 1)  S(I',J) = sum_I LB(I',I) Et(J,I)^T
 //   mode 3  (LB first, product 2)  W(I',J') -= sum_J S(I',J) LA(J',J)^T
+//   mode 4  dense: C(ci = rlo + y, cj = olo + x) over the K blocks 0 .. L-1,
+//           cut at ci (H = 1: A lower triangular) or at cj (H = 2: B lower);
+//           the cross update of a split solve
 // Grid: x = offset along the band (from olo), y = row index (from rlo).
+constexpr int BW_STORE = 0, BW_SUB = 1;  // BandArgs::subtract: C = acc, C -= acc
 struct BandArgs {
     const float *A, *B;
     float *C;
@@ -776,10 +782,13 @@ __device__ inline bool band_tile(const BandArgs &g, int bx, int by, int &ci, int
         const int J = row, Ip = K - J + o;
         if (Ip < 0 || Ip >= g.M) return false;
         ci = Ip; cj = J; klo = max(0, K - J); khi = min(Ip, K + H - 1 - J);
-    } else {
+    } else if (g.mode == 3) {
         const int Ip = row, Jp = K + H + o - Ip;
         if (Jp < 0 || Jp >= g.N) return false;
         ci = Ip; cj = Jp; klo = max(0, K - Ip); khi = min(Jp, K + H - 1);
+    } else {
+        ci = row; cj = o; klo = 0;
+        khi = H == 1 ? min(g.L - 1, ci) : (H == 2 ? min(g.L - 1, cj) : g.L - 1);
     }
     return klo <= khi;
 }
@@ -1475,7 +1484,11 @@ size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     double *part = cv.take<double>(NPART);
     float *Cd = cv.take<float>(mp * np);
     float *Cr = cv.take<float>(mp * np);
-    const int nctr = std::max(1, shape_info((int)(mp / TB), (int)(np / TB)).side_ops);
+    // counters for the plan of the whole grid and of the parts of a split solve
+    const int M = (int)(mp / TB), N = (int)(np / TB);
+    int nctr = std::max(1, shape_info(M, N).side_ops);
+    if (N >= 2) nctr = std::max({nctr, shape_info(M, N / 2).side_ops, shape_info(M, N - N / 2).side_ops});
+    if (M >= 2) nctr = std::max({nctr, shape_info(M / 2, N).side_ops, shape_info(M - M / 2, N).side_ops});
     int *ctr = cv.take<int>(nctr);
     if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part, ctr, nctr};
     return cv.used;
@@ -1580,15 +1593,124 @@ struct Solve {
     const float *W, *LA, *LB;
     int64_t m, n, mp, np;
     int M, N, order, qkind, qbits, qmin, qmax;
-    int mse;  // per-row scale shrink by MSE search
+    int mse;    // per-row scale shrink by MSE search
+    int split;  // SPLIT_NONE, SPLIT_COLS, SPLIT_ROWS: the hybrid schedule's top-level split
     int8_t *codes;
     float *scales, *zeros, *V, *E;
+    int64_t ldo;  // row stride of codes, V, E (the full n; a part's m, n are its bounds)
     double *sum_e2;
     int32_t *dev_status;
     Buffers b;
 };
 
+// The hybrid schedule (BaKron-recursive's row / column split at the top level,
+// Algorithm 6 below; pith.science review of arXiv 2608.06291, "Circularity
+// Check": the recurrence F(m,n) - F(m,n1) - F(m,n2) = 2 m n1 n2 of Appendix C).
+// A column split at tile J1 solves the columns 0 .. J1-1, applies their
+// updates to the rest, W2 -= LB E1 LA21^T, then solves the columns J1 ..; a
+// row split at I1 likewise with W2 -= LB21 E1 LA^T.  Both visit the entries
+// in an order that extends the product order, so the result is the same
+// (Theorem 3.2, "Core claim").
+constexpr int SPLIT_NONE = 0, SPLIT_COLS = 1, SPLIT_ROWS = 2;
+
+// The tile block rows I0 .. I0+Ms-1, columns J0 .. J0+Ns-1 of a solve, as a
+// solve of its own over the same buffers (pointers moved to the block, strides
+// kept).
+Solve part_view(const Solve &sv, int I0, int J0, int Ms, int Ns) {
+    Solve p = sv;
+    const int64_t r0 = (int64_t)I0 * TB, c0 = (int64_t)J0 * TB;
+    p.M = Ms;
+    p.N = Ns;
+    p.m = std::min<int64_t>(sv.m - r0, (int64_t)Ms * TB);
+    p.n = std::min<int64_t>(sv.n - c0, (int64_t)Ns * TB);
+    p.b.Wp += r0 * sv.np + c0;
+    p.b.Cd += r0 * sv.np + c0;
+    p.b.Cr += r0 * sv.np + c0;
+    p.b.LAp += c0 * sv.np + c0;
+    p.b.LBp += r0 * sv.mp + r0;
+    p.b.sc += r0;
+    p.b.zp += r0;
+    p.b.Ebuf += sv.order == BAKRON_ORDER_LA_FIRST ? r0 * sv.np + c0 : c0 * sv.mp + r0;
+    p.codes += r0 * sv.ldo + c0;
+    if (p.V) p.V += r0 * sv.ldo + c0;
+    if (p.E) p.E += r0 * sv.ldo + c0;
+    return p;
+}
+
+// the parts of a solve: (I0, J0, M, N) of each, in the order they run
+int solve_parts(const Solve &sv, int part[2][4]) {
+    if (sv.split == SPLIT_COLS) {
+        const int J1 = sv.N / 2;
+        part[0][0] = 0; part[0][1] = 0; part[0][2] = sv.M; part[0][3] = J1;
+        part[1][0] = 0; part[1][1] = J1; part[1][2] = sv.M; part[1][3] = sv.N - J1;
+        return 2;
+    }
+    if (sv.split == SPLIT_ROWS) {
+        const int I1 = sv.M / 2;
+        part[0][0] = 0; part[0][1] = 0; part[0][2] = I1; part[0][3] = sv.N;
+        part[1][0] = I1; part[1][1] = 0; part[1][2] = sv.M - I1; part[1][3] = sv.N;
+        return 2;
+    }
+    part[0][0] = 0; part[0][1] = 0; part[0][2] = sv.M; part[0][3] = sv.N;
+    return 1;
+}
+
+// events a solve's plans need (its parts run one after the other)
+int solve_events(const Solve &sv) {
+    int part[2][4], ev = 0;
+    const int np_ = solve_parts(sv, part);
+    for (int k = 0; k < np_; ++k) ev = std::max(ev, shape_info(part[k][2], part[k][3]).plan.events);
+    return ev;
+}
+
 int32_t launch_band(const Solve &sv, const Op &op, int *ctr, hipStream_t stream, int *launched);
+
+// One dense product of a split solve's cross update (band_gemm_kernel mode 4):
+// C (rows x cols tiles) =|-= A B^T over kt K blocks, cut at the row (tri 1:
+// A lower triangular) or the column (tri 2: B lower triangular).
+int32_t launch_dense(const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                     int64_t ldc, int rows, int cols, int kt, int tri, int subtract,
+                     hipStream_t stream) {
+    if (rows <= 0 || cols <= 0 || kt <= 0) return BAKRON_OK;
+    BandArgs g{A, B, C, lda, ldb, ldc, 4, 0, kt, tri, rows, cols, 0, subtract, rows, 0, cols};
+    hipLaunchKernelGGL(band_gemm_kernel, dim3(cols, (rows + 7) & ~7), dim3(256), 0, stream, g);
+    BK_LAUNCH_CHECK("band_gemm_kernel");
+    return BAKRON_OK;
+}
+
+// The cross update of a split solve, between its parts: the first part's E
+// applied to the second part's W (the part at tile row I1 or column J1; T of
+// depth 0 holds the intermediate product).
+int32_t cross_update(const Solve &sv, int I1, int J1, hipStream_t stream) {
+    const Buffers &b = sv.b;
+    const int64_t mp = sv.mp, np = sv.np, r1 = (int64_t)I1 * TB, c1 = (int64_t)J1 * TB;
+    const int M = sv.M, N = sv.N;
+    float *T = b.Tbuf;
+    const bool la_first = sv.order == BAKRON_ORDER_LA_FIRST;
+    int32_t st;
+    if (sv.split == SPLIT_COLS) {  // W2 -= LB E1 LA21^T
+        if (la_first) {            // Tt(J', I) = sum_J LA21(J', J) E(I, J); W2 -= LB Tt^T
+            st = launch_dense(b.LAp + c1 * np, np, b.Ebuf, np, T, mp, N - J1, M, J1, 0, BW_STORE, stream);
+            if (st == BAKRON_OK)
+                st = launch_dense(b.LBp, mp, T, mp, b.Wp + c1, np, M, N - J1, M, 1, BW_SUB, stream);
+        } else {                   // S(I', J) = sum_I LB(I', I) E(I, J); W2 -= S LA21^T
+            st = launch_dense(b.LBp, mp, b.Ebuf, mp, T, np, M, J1, M, 1, BW_STORE, stream);
+            if (st == BAKRON_OK)
+                st = launch_dense(T, np, b.LAp + c1 * np, np, b.Wp + c1, np, M, N - J1, J1, 0, BW_SUB, stream);
+        }
+    } else {                       // W2 -= LB21 E1 LA^T
+        if (la_first) {            // Tt(J', I) = sum_J LA(J', J) E(I, J), I < I1; W2 -= LB21 Tt^T
+            st = launch_dense(b.LAp, np, b.Ebuf, np, T, mp, N, I1, N, 1, BW_STORE, stream);
+            if (st == BAKRON_OK)
+                st = launch_dense(b.LBp + r1 * mp, mp, T, mp, b.Wp + r1 * np, np, M - I1, N, I1, 0, BW_SUB, stream);
+        } else {                   // S(I', J) = sum_{I < I1} LB21(I', I) E(I, J); W2 -= S LA^T
+            st = launch_dense(b.LBp + r1 * mp, mp, b.Ebuf, mp, T, np, M - I1, N, I1, 0, BW_STORE, stream);
+            if (st == BAKRON_OK)
+                st = launch_dense(T, np, b.LAp, np, b.Wp + r1 * np, np, M - I1, N, N, 2, BW_SUB, stream);
+        }
+    }
+    return st;
+}
 
 // Enqueues the whole solve.  With `side` (and `sync`, the plan's events),
 // deferred band products run on `side`, forked from and joined into `stream`;
@@ -1613,7 +1735,6 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
         if (s_ != BAKRON_OK) return s_; \
     } while (0)
     const Buffers &b = sv.b;
-    const int M = sv.M, N = sv.N;
     const int64_t m = sv.m, n = sv.n, mp = sv.mp, np = sv.np;
     BK_MARK(-1);
     hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, sv.W, m, n,
@@ -1635,39 +1756,54 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     const auto aligned = [](const void *p, uintptr_t to) {
         return (reinterpret_cast<uintptr_t>(p) & (to - 1)) == 0;
     };
-    const int out_vec = n % 4 == 0 && aligned(sv.codes, 4) && aligned(sv.V, 16) && aligned(sv.E, 16);
-    LeafArgs la{b.Wp, b.Ebuf, b.LAp, b.LBp, b.sc, b.zp, mp, np, M, N, sv.order, sv.qmin, sv.qmax,
-                sv.codes, sv.V, sv.E, m, n, sv.dev_status, b.Cd, b.Cr, out_vec};
-    const Plan &plan = shape_info(M, N).plan;
-    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, stream, b.ctr, b.nctr);
-    BK_LAUNCH_CHECK("zero_i32_kernel");
-    int side_k = 0;
-    for (const Op &op : plan.ops) {
-        if (op.kind == OP_RECORD || op.kind == OP_WAIT) {
-            if (!side) continue;
-            hipStream_t st = op.side ? side : stream;
-            if (op.kind == OP_RECORD) BK_HIP_CHECK(hipEventRecord((*sync)[op.ev], st));
-            else BK_HIP_CHECK(hipStreamWaitEvent(st, (*sync)[op.ev], 0));
-            continue;
+    // the parts (one without a split) and, between them, the cross update
+    int part[2][4];
+    const int nparts = solve_parts(sv, part);
+    for (int k = 0; k < nparts; ++k) {
+        if (k == 1) {
+            const int32_t st = cross_update(sv, part[1][0], part[1][1], stream);
+            if (st != BAKRON_OK) return st;
+            BK_MARK(2);
         }
-        const Node &nd = op.nd;
-        if (op.kind == OP_LEAF) {
-            const int Ilo = std::max(0, nd.K - N + 1), Ihi = std::min(M - 1, nd.K);
-            if (sv.qkind == BAKRON_Q_ASYM)
-                hipLaunchKernelGGL(leaf_kernel<true>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream,
-                                   la, nd.K, nd.flags);
-            else
-                hipLaunchKernelGGL(leaf_kernel<false>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0, stream,
-                                   la, nd.K, nd.flags);
-            BK_LAUNCH_CHECK("leaf_kernel");
-            BK_MARK(1);
-            continue;
+        const Solve pv = part_view(sv, part[k][0], part[k][1], part[k][2], part[k][3]);
+        const Buffers &pb = pv.b;
+        const int PM = pv.M, PN = pv.N;
+        const int out_vec = sv.ldo % 4 == 0 && aligned(pv.codes, 4) && aligned(pv.V, 16) &&
+                            aligned(pv.E, 16);
+        LeafArgs la{pb.Wp, pb.Ebuf, pb.LAp, pb.LBp, pb.sc, pb.zp, mp, np, PM, PN, sv.order,
+                    sv.qmin, sv.qmax, pv.codes, pv.V, pv.E, pv.m, pv.n, sv.dev_status, pb.Cd, pb.Cr,
+                    out_vec, sv.ldo};
+        const Plan &plan = shape_info(PM, PN).plan;
+        hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, stream, b.ctr, b.nctr);
+        BK_LAUNCH_CHECK("zero_i32_kernel");
+        int side_k = 0;
+        for (const Op &op : plan.ops) {
+            if (op.kind == OP_RECORD || op.kind == OP_WAIT) {
+                if (!side) continue;
+                hipStream_t st = op.side ? side : stream;
+                if (op.kind == OP_RECORD) BK_HIP_CHECK(hipEventRecord((*sync)[op.ev], st));
+                else BK_HIP_CHECK(hipStreamWaitEvent(st, (*sync)[op.ev], 0));
+                continue;
+            }
+            const Node &nd = op.nd;
+            if (op.kind == OP_LEAF) {
+                const int Ilo = std::max(0, nd.K - PN + 1), Ihi = std::min(PM - 1, nd.K);
+                if (sv.qkind == BAKRON_Q_ASYM)
+                    hipLaunchKernelGGL(leaf_kernel<true>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0,
+                                       stream, la, nd.K, nd.flags);
+                else
+                    hipLaunchKernelGGL(leaf_kernel<false>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0,
+                                       stream, la, nd.K, nd.flags);
+                BK_LAUNCH_CHECK("leaf_kernel");
+                BK_MARK(1);
+                continue;
+            }
+            int *ctr = op.side ? b.ctr + side_k++ : nullptr;
+            int launched = 0;
+            const int32_t st = launch_band(pv, op, ctr, op.side && side ? side : stream, &launched);
+            if (st != BAKRON_OK) return st;
+            if (launched) BK_MARK(op.side ? 4 : 2);
         }
-        int *ctr = op.side ? b.ctr + side_k++ : nullptr;
-        int launched = 0;
-        const int32_t st = launch_band(sv, op, ctr, op.side && side ? side : stream, &launched);
-        if (st != BAKRON_OK) return st;
-        if (launched) BK_MARK(op.side ? 4 : 2);
     }
     if (sv.sum_e2) {
         hipLaunchKernelGGL(sumsq_partial_kernel, dim3(NPART), dim3(256), 0, stream, b.Ebuf,
@@ -1685,7 +1821,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
 // buffers' current contents.  At most kGraphCache entries; the least recently
 // used one is dropped.
 struct GraphKey {
-    int dev, order, qkind, qbits, mse;
+    int dev, order, qkind, qbits, mse, split;
     int64_t m, n;
     const void *p[12];
     bool operator<(const GraphKey &o) const {
@@ -1694,6 +1830,7 @@ struct GraphKey {
         if (qkind != o.qkind) return qkind < o.qkind;
         if (qbits != o.qbits) return qbits < o.qbits;
         if (mse != o.mse) return mse < o.mse;
+        if (split != o.split) return split < o.split;
         if (m != o.m) return m < o.m;
         if (n != o.n) return n < o.n;
         for (int k = 0; k < 12; ++k)
@@ -1738,7 +1875,7 @@ int32_t make_stream(hipStream_t *s) {
 
 // Finds or builds the graph for `sv`; returns it through `exec`.
 int32_t graph_for(const Solve &sv, int dev, const void *ws, hipGraphExec_t *exec) {
-    GraphKey key{dev, sv.order, sv.qkind, sv.qbits, sv.mse, sv.m, sv.n,
+    GraphKey key{dev, sv.order, sv.qkind, sv.qbits, sv.mse, sv.split, sv.m, sv.n,
                  {sv.W, sv.LA, sv.LB, sv.codes, sv.scales, sv.zeros, sv.V, sv.E, sv.sum_e2,
                   sv.dev_status, ws, nullptr}};
     std::lock_guard<std::mutex> lock(g_graph_mu);
@@ -1751,7 +1888,7 @@ int32_t graph_for(const Solve &sv, int dev, const void *ws, hipGraphExec_t *exec
     DevStreams &ds = g_dev[dev];
     int32_t st = make_stream(&ds.cap);
     if (st == BAKRON_OK) st = make_stream(&ds.cap_side);
-    if (st == BAKRON_OK) st = grow_events(ds.cap_ev, shape_info(sv.M, sv.N).plan.events);
+    if (st == BAKRON_OK) st = grow_events(ds.cap_ev, solve_events(sv));
     if (st != BAKRON_OK) return st;
     hipStream_t cs = ds.cap;
     BK_HIP_CHECK(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
@@ -1892,9 +2029,14 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
                (long long)m, (long long)n);
     BK_REQUIRE(valid_quantizer(qkind, qbits), "unsupported quantizer kind=%d bits=%d", qkind, qbits);
     BK_REQUIRE((flags & ~(BAKRON_ORDER_MASK | BAKRON_FLAG_PHASE_TIMING | BAKRON_FLAG_NO_GRAPH |
-                          BAKRON_FLAG_MSE_SCALE)) == 0 &&
+                          BAKRON_FLAG_MSE_SCALE | BAKRON_FLAG_SPLIT_COLS | BAKRON_FLAG_SPLIT_ROWS)) == 0 &&
                    (flags & BAKRON_ORDER_MASK) != 3,
                "unknown flags 0x%x", flags);
+    BK_REQUIRE(!((flags & BAKRON_FLAG_SPLIT_COLS) && (flags & BAKRON_FLAG_SPLIT_ROWS)),
+               "BAKRON_FLAG_SPLIT_COLS and BAKRON_FLAG_SPLIT_ROWS exclude each other");
+    BK_REQUIRE(!((flags & (BAKRON_FLAG_SPLIT_COLS | BAKRON_FLAG_SPLIT_ROWS)) &&
+                 (flags & BAKRON_FLAG_PHASE_TIMING)),
+               "BAKRON_FLAG_PHASE_TIMING times the unsplit schedule only (no BAKRON_FLAG_SPLIT_*)");
     const size_t need = bakron_quantize_workspace_size(m, n, qkind, qbits);
     if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
         set_error("workspace needs %zu bytes at 256-byte alignment (got %zu at %p)", need,
@@ -1921,7 +2063,12 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     else if (qkind == BAKRON_Q_ASYM) { sv.qmin = 0; sv.qmax = (1 << qbits) - 1; }
     else { sv.qmin = -128; sv.qmax = 127; }
     sv.codes = codes; sv.scales = scales; sv.zeros = zeros; sv.V = V; sv.E = E;
+    sv.ldo = n;
     sv.sum_e2 = sum_e2; sv.dev_status = dev_status;
+    // a split of a one-tile dimension leaves nothing to split
+    sv.split = (flags & BAKRON_FLAG_SPLIT_COLS) && sv.N >= 2   ? SPLIT_COLS
+               : (flags & BAKRON_FLAG_SPLIT_ROWS) && sv.M >= 2 ? SPLIT_ROWS
+                                                               : SPLIT_NONE;
     carve(ws, sv.mp, sv.np, &sv.b);
 
     if (flags & BAKRON_FLAG_PHASE_TIMING) {
@@ -1964,7 +2111,7 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
             ds = &g_dev[dev];
         }
         st = make_stream(&ds->side);
-        if (st == BAKRON_OK) st = grow_events(ds->ev, si.plan.events);
+        if (st == BAKRON_OK) st = grow_events(ds->ev, solve_events(sv));
         if (st != BAKRON_OK) return st;
         return enqueue_solve(sv, stream, ds->side, &ds->ev, nullptr, nullptr);
     }
