@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="c3")
-    p.add_argument("--cpu-sample", type=int, default=896,
+    p.add_argument("--cpu-sample", type=int, default=1024,
                    help="edge of the leading block timed with the CPU oracle (0 = skip)")
     p.add_argument("--order", type=int, default=0)
     p.add_argument("--antidiag", action="store_true",
