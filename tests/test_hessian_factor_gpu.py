@@ -34,7 +34,7 @@ def test_hessian_matches_oracle(bk, N, d):
     assert np.allclose(Hg, Hg.T, rtol=0, atol=1e-6 * np.max(np.abs(Ho)))
 
 
-@pytest.mark.parametrize("d", [1, 7, 64, 65, 200, 512])
+@pytest.mark.parametrize("d", [1, 7, 64, 65, 200, 512, 1000, 2048])
 def test_factor_matches_oracle(bk, d):
     g = np.random.default_rng(d)
     X = g.standard_normal((2 * d + 8, d)).astype(np.float32)
