@@ -525,9 +525,12 @@ __device__ __forceinline__ void leaf_helpers(const int hw, const int lane) {
 //   to (I+1, J):  LB(I+1,I) (E(I,J) LA(J,J)^T)
 //   to (I, J+1):  LB(I,I) (E(I,J) LA(J+1,J)^T),
 // into the workspace, and the leaf of diagonal K+1 subtracts them while it
-// loads its W tile.  fp32 MFMA on 32 x 32 quadrants (waves 0-3, one per
-// SIMD); lane l supplies row l % 32 of both operands and the k half l / 32; the
-// triangular diagonal blocks cut the k range of the quadrants that allow it.
+// loads its W tile.  E(I,J) LA(J,J)^T is the sweep's Z (each step forms
+// z = E[r][c] LA[c][c] + sum_{k<c} E[r][k] LA[c][k]), which lf_Z already holds
+// transposed; the other three products run on fp32 MFMA in 32 x 32 quadrants
+// (waves 0-3, one per SIMD); lane l supplies row l % 32 of both operands and
+// the k half l / 32; the triangular diagonal blocks cut the k range of the
+// quadrants that allow it.
 
 // acc += A[i][k] B[j][k]^T over k < KN for the 32 x 32 block; fa(i, k), fb(j, k)
 // return the float4 at k .. k+3 of row i (j) of the block.
@@ -549,27 +552,23 @@ __device__ __forceinline__ float4 lds4(const float *base, int stride, int row, i
     return *reinterpret_cast<const float4 *>(base + row * stride + k);
 }
 
-// waves 0-3: quadrant (w >> 1, w & 1).  Phase 1 stores U^T and V^T (stride
-// GP) in lf_Z and in the skewed-W area, both free once the sweep's outputs are
-// written; phase 2 writes the contributions.
+// waves 0-3: quadrant (w >> 1, w & 1).  Phase 1 stores V^T (stride GP) in
+// the skewed-W area, free once the sweep's outputs are written; phase 2 writes
+// the contributions (U^T is the sweep's Z^T in lf_Z, stride LP).
 __device__ __forceinline__ void leaf_push(const LeafArgs &a, int I, int J, int w, bool phase2) {
     const int lane = threadIdx.x & 63;
     const int qr = w >> 1, qc = w & 1;
     const bool down = I + 1 < a.M, right = J + 1 < a.N;
     const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
     const int rb = 32 * qr, cb = 32 * qc;
-    float *Ut = lf_Z, *Vt = lf_Wk;
+    const float *Ut = lf_Z;
+    float *Vt = lf_Wk;
     floatx16 acc, acc2;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = acc2[v] = 0.0f;
     if (!phase2) {
-        if (down) {  // U = E LA(J,J)^T
-            auto fa = [&](int i, int k) { return lds4(lf_E, LP, rb + i, k); };
-            auto fb = [&](int j, int k) { return lds4(lf_A, LP, cb + j, k); };
-            if (qc) mfma_block<64>(acc, fa, fb);
-            else mfma_block<32>(acc, fa, fb);
-        }
-        if (right) {  // V = E LA(J+1,J)^T
+        if (!right) return;
+        {  // V = E LA(J+1,J)^T
             auto fa = [&](int i, int k) { return lds4(lf_E, LP, rb + i, k); };
             auto fb = [&](int j, int k) { return lds4(lf_P, GP, cb + j, k); };
             mfma_block<64>(acc2, fa, fb);
@@ -578,13 +577,12 @@ __device__ __forceinline__ void leaf_push(const LeafArgs &a, int I, int J, int w
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int rr = rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cc = cb + (lane & 31);
-            Ut[cc * GP + rr] = acc[v];
             Vt[cc * GP + rr] = acc2[v];
         }
     } else {
-        if (down) {  // LB(I+1,I) U
+        if (down) {  // LB(I+1,I) U with U^T = Z^T
             auto fa = [&](int i, int k) { return lds4(lf_P + TB * GP, GP, rb + i, k); };
-            auto fb = [&](int j, int k) { return lds4(Ut, GP, cb + j, k); };
+            auto fb = [&](int j, int k) { return lds4(Ut, LP, cb + j, k); };
             mfma_block<64>(acc, fa, fb);
         }
         if (right) {  // LB(I,I) V
