@@ -15,9 +15,10 @@
 //   G22 -= C21 C21^T                 (lower tiles only)
 //   (C22, X22) = recurse(G22)
 //   X21  = -X22 (C21 X11)
-// down to 64 x 64 blocks, which one workgroup factors and inverts in LDS.  The
-// products run on fp64 MFMA (v_mfma_f64_16x16x4f64) in 64 x 64 output tiles,
-// skipping the k blocks where a triangular operand is zero.
+// down to 64 x 64 blocks, which one workgroup factors and inverts with the
+// block held in registers (base_kernel).  The products run on fp64 MFMA
+// (v_mfma_f64_16x16x4f64) in 64 x 64 output tiles, skipping the k blocks where
+// a triangular operand is zero.
 #include <vector>
 
 #include "common.hpp"
