@@ -12,7 +12,7 @@ import pytest
 import oracle
 from two_sided_gptq_amd import synth
 
-from test_quantize_gpu import _check_parity, _factors
+from test_quantize_gpu import _check_parity, _factors, _mse_params
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -27,13 +27,13 @@ def bk():
     return bakron
 
 
-def _gpu_split(bk, W, LA, LB, kind, bits, order, split, graph=True):
+def _gpu_split(bk, W, LA, LB, kind, bits, order, split, graph=True, mse=False):
     dev = torch.device("cuda:0")
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     out = bk.quantize(torch.from_numpy(W).to(dev), torch.from_numpy(LA).to(dev),
                       torch.from_numpy(LB).to(dev), kind=kind, bits=bits, order=order,
                       want_V=True, want_E=True, want_sum=True, dev_status=status, split=split,
-                      graph=graph)
+                      graph=graph, mse=mse)
     torch.cuda.synchronize()
     res = {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
     res["status"] = int(status.item())
@@ -59,6 +59,21 @@ def test_split_parity_quantizers(bk, kind, bits):
     for split in ("cols", "rows"):
         res = _gpu_split(bk, W, LA, LB, kind, bits, 0, split)
         _check_parity(W, A, B, LA, LB, kind, bits, res, f"kind {kind} bits {bits} {split}")
+
+
+def test_split_with_mse_scale_search(bk):
+    # the scale search runs once on the whole W, before the parts; the split
+    # solve then matches the naive oracle on those parameters
+    m, n = 200, 300
+    W, X, Y = synth.custom(m, n, 9700, outliers=6)
+    A, B, LA, LB = _factors(X, Y, m)
+    for split in ("cols", "rows"):
+        print(f"[split] mse {split}", flush=True)
+        res = _gpu_split(bk, W, LA, LB, synth.ASYM, 4, 0, split, mse=True)
+        zeros = res["zeros"] if res["zeros"] is not None else np.zeros(m, np.float32)
+        s, z, kb, ndiff = _mse_params(W, synth.ASYM, 4, res["scales"], zeros)
+        assert ndiff <= 2
+        _check_parity(W, A, B, LA, LB, synth.ASYM, 4, res, f"mse {split}", sz=(s, z))
 
 
 @pytest.mark.parametrize("split", ["cols", "rows"])
