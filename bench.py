@@ -10,7 +10,9 @@ bakron_factor on the synthetic samples (untimed preparation).
 Prints one JSON line.  Besides the contract fields it carries
   roofline      for the dominant kernel (band GEMM: fp32 MFMA peak), with
                 algorithmic flops / average launch duration from HIP events
-                recorded inside the library on the solver's stream
+                recorded inside the library on the solver's stream, and the
+                MFMA utilisation from the committed counter summary (fp32
+                MFMA flops counted per dispatch over that same duration)
   leaf          the leaf phase: HBM bytes per launch, launches, in-kernel steps
   cpu_baseline  the fp64 oracle (BaKron-naive) on a bounded leading block of
                 the same problem, on this host's cores
@@ -170,11 +172,17 @@ def main():
     # summary, null unless it was taken from the current kernel source
     from two_sided_gptq_amd import profsum
     traffic = profsum.read_traffic(PROFILE_MD, "band_gemm_kernel")
+    # MFMA utilisation from the same summary's counters: fp32 MFMA flops the
+    # hardware counted per dispatch (executed, so the zero halves of triangular
+    # blocks included) over this run's average launch duration, against the peak
+    counted = profsum.read_figure(PROFILE_MD, "mfma_flops_per_dispatch", "band_gemm_kernel")
+    mfma_util = counted / gemm_avg_s / 1e12 / FP32_MFMA_PEAK_TFLOPS if counted else None
     roofline = {"kernel": "band_gemm_kernel", "bound": "mfma", "achieved": gemm_tflops,
                 "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": gemm_tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": traffic,
                 "alg_flops_per_launch": gemm_alg_per_launch, "avg_launch_ms": gemm_avg_s * 1e3,
-                "launches": band_launches}
+                "launches": band_launches, "counted_mfma_flops_per_launch": counted,
+                "mfma_util_counted": mfma_util}
 
     result = {
         "metric": "weight entries quantized/sec at 4096x4096 INT4; % of fp32 MFMA peak",

@@ -5,12 +5,23 @@
 DIR of --trace holds `bench_kernel_trace.csv` and `bench_kernel_stats.csv`
 (`rocprofv3 --kernel-trace --stats --output-format csv -o bench`); DIR of --pmc
 holds `FETCH_SIZE/run_counter_collection.csv` and `WRITE_SIZE/...` (one
-`rocprofv3 --pmc <counter> -o run` pass each, with `bench.py --copy-probe`).
+`rocprofv3 --pmc <counter> -o run` pass each, with `bench.py --copy-probe`)
+and, when present, `MFMA/...` (SQ_VALU_MFMA_BUSY_CYCLES,
+SQ_INSTS_VALU_MFMA_MOPS_F32 and GRBM_GUI_ACTIVE in one pass) and `MfmaUtil/...`
+(rocprofv3's derived utilisation, a pass of its own).
 
 HBM bytes per dispatch: FETCH_SIZE and WRITE_SIZE (KiB) are each scaled so that
 the 1 GiB device copy the benchmark runs with --copy-probe reads and writes
-exactly 1 GiB.  The summary records a hash of the kernel source; `bench.py`
-reports the measured traffic only while the source still has that hash.
+exactly 1 GiB.  MFMA work per dispatch: SQ_INSTS_VALU_MFMA_MOPS_F32 counts
+fp32 MFMA flops in units of 512; SQ_VALU_MFMA_BUSY_CYCLES counts the cycles
+each SIMD's matrix unit is busy (64 per v_mfma_f32_32x32x2f32, 4096 flops, so
+the two agree at 64 flops per busy cycle, the fp32 matrix rate of one SIMD).
+The busy share of a kernel is its busy cycles over 1024 SIMDs x its average
+duration x 2.4 GHz, i.e. its counted MFMA rate over the fp32 MFMA peak.
+rocprofv3's MfmaUtil divides by GRBM_GUI_ACTIVE instead, which for dispatches
+of some tens of microseconds also spans the counter collection around them.
+The summary records a hash of the kernel source; `bench.py` reports the
+measured figures only while the source still has that hash.
 """
 from __future__ import annotations
 
@@ -25,6 +36,9 @@ import statistics
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(HERE, "csrc", "quantize.hip")
 COPY_BYTES = 1 << 30
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+MFMA_KERNELS = ("band_gemm_kernel", "band_side_kernel", "leaf_kernel<false>")
 
 
 def source_hash(path: str = KERNEL_SOURCE) -> str:
@@ -66,7 +80,8 @@ def _table(out, win, title):
     out.append("")
 
 
-def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> str:
+def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str,
+              mfma_command: str = "") -> str:
     out = []
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_trace.csv"))))
     graph_win, timing_win, replay_win = _windows(rows)
@@ -78,7 +93,9 @@ def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> s
     out.append("\n### rocprofv3 --stats (whole command)\n")
     out.append("| kernel | calls | average ns | % |")
     out.append("|---|---|---|---|")
+    avg_ns = {}
     for r in csv.DictReader(open(os.path.join(trace_dir, "bench_kernel_stats.csv"))):
+        avg_ns[short_name(r["Name"])] = float(r["AverageNs"])
         out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                    f"{float(r['Percentage']):.2f} |")
     # counters
@@ -105,17 +122,61 @@ def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str) -> s
         b = (f * f_scale + w * w_scale) * 1024
         traffic[k] = b
         out.append(f"| {k} | {len(d['FETCH_SIZE'])} | {f:.1f} | {w:.1f} | {b:.4g} |")
+    mfma = _mfma_section(out, pmc_dir, avg_ns, mfma_command)
     out.append("\nMachine-readable (read by bench.py):\n")
     out.append(f"    source_sha256_16: {source_hash()}")
-    for k in ("band_gemm_kernel", "band_side_kernel", "leaf_kernel<false>"):
+    for k in MFMA_KERNELS:
         if k in traffic:
             out.append(f"    traffic_bytes_per_dispatch: {k} {traffic[k]:.6g}")
+    for k in MFMA_KERNELS:
+        if k in mfma:
+            out.append(f"    mfma_flops_per_dispatch: {k} {mfma[k]:.6g}")
     return "\n".join(out) + "\n"
 
 
-def read_traffic(md_path: str, kernel: str):
-    """Bytes per dispatch of `kernel` from a summary, or None when the summary is
-    missing or was taken from a different kernel source."""
+def _per_kernel(path):
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        vals[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return vals
+
+
+def _mfma_section(out, pmc_dir, avg_ns, command):
+    """Counted fp32 MFMA flops and busy cycles per dispatch of each kernel that
+    issues MFMA; returns {kernel: counted flops per dispatch}."""
+    path = os.path.join(pmc_dir, "MFMA", "run_counter_collection.csv")
+    if not os.path.exists(path):
+        return {}
+    vals = _per_kernel(path)
+    upath = os.path.join(pmc_dir, "MfmaUtil", "run_counter_collection.csv")
+    util = _per_kernel(upath) if os.path.exists(upath) else {}
+    out.append(f"\n### MFMA work (counter command: `{command}`)\n")
+    out.append("Busy share = busy cycles / (1024 SIMDs x kernel average duration from the trace x 2.4 GHz).\n")
+    out.append("| kernel | dispatches | fp32 MFMA flops (MOPS_F32 x 512) | MFMA busy cycles | "
+               "flops / busy cycle / SIMD | avg us (trace) | busy share | rocprofv3 MfmaUtil % |")
+    out.append("|---|---|---|---|---|---|---|---|")
+    flops = {}
+    for k, d in vals.items():
+        mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_F32")
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        if not mops or not busy or statistics.mean(mops) == 0:
+            continue  # no fp32 MFMA (the factor's fp64 products count elsewhere)
+        f = statistics.mean(mops) * 512
+        b = statistics.mean(busy)
+        flops[k] = f
+        avg = avg_ns.get(k)
+        share = f"{b / (SIMDS * avg * 1e-9 * CLOCK_HZ):.3f}" if avg else "-"
+        u = util.get(k, {}).get("MfmaUtil")
+        out.append(f"| {k} | {len(mops)} | {f:.4g} | {b:.4g} | {f / b:.1f} | "
+                   f"{avg / 1e3 if avg else float('nan'):.2f} | {share} | "
+                   f"{statistics.mean(u) if u else float('nan'):.1f} |")
+    return flops
+
+
+def read_figure(md_path: str, key: str, kernel: str):
+    """A per-dispatch figure (`key`: traffic_bytes_per_dispatch or
+    mfma_flops_per_dispatch) of `kernel` from a summary, or None when the
+    summary is missing, lacks it or was taken from a different kernel source."""
     try:
         text = open(md_path).read()
     except OSError:
@@ -123,8 +184,13 @@ def read_traffic(md_path: str, kernel: str):
     m = re.search(r"source_sha256_16: (\w+)", text)
     if not m or m.group(1) != source_hash():
         return None
-    m = re.search(r"traffic_bytes_per_dispatch: " + re.escape(kernel) + r" ([\d.e+]+)", text)
+    m = re.search(re.escape(key) + r": " + re.escape(kernel) + r" ([\d.e+]+)", text)
     return float(m.group(1)) if m else None
+
+
+def read_traffic(md_path: str, kernel: str):
+    """HBM bytes per dispatch of `kernel` (see read_figure)."""
+    return read_figure(md_path, "traffic_bytes_per_dispatch", kernel)
 
 
 def main():
@@ -137,8 +203,12 @@ def main():
     p.add_argument("--pmc-command", default="rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv "
                    "-d <pmc dir>/<counter> -o run -- python3 bench.py --steps 1 --warmup 0 "
                    "--cpu-sample 0 --copy-probe")
+    p.add_argument("--mfma-command", default="rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                   "SQ_INSTS_VALU_MFMA_MOPS_F32 GRBM_GUI_ACTIVE (then, in a run of its own, MfmaUtil) "
+                   "--output-format csv -d <pmc dir>/<MFMA|MfmaUtil> -o run -- python3 bench.py "
+                   "--steps 1 --warmup 0 --cpu-sample 0")
     a = p.parse_args()
-    text = summarise(a.trace, a.pmc, a.command, a.pmc_command)
+    text = summarise(a.trace, a.pmc, a.command, a.pmc_command, a.mfma_command)
     with open(a.out, "w") as f:
         f.write(text)
     print(a.out)
