@@ -246,7 +246,7 @@ __device__ inline float dot4(const float4 a, const float4 b, float s) {
 // Wave 0 is the chain: lane r owns row r for the whole sweep (it is active at
 // steps r .. r+63) and rounds entry (r, d - r) at step d.  The two dots are
 // split at a boundary s0 that moves every LJ steps: terms produced before
-// step s0 (the bulk) come precomputed from the three helper waves, the rest
+// step s0 (the bulk) come precomputed by the helper waves, the rest
 // (the last LJ..2LJ-1 terms of each dot) the chain adds itself:
 //   row direction     its own last errors E[r][c-j], kept in registers;
 //   column direction  Z[r-j][c], which lane r-j produced j steps ago.  Lane r
@@ -267,11 +267,8 @@ constexpr int LJ = 4;                               // chain steps per block
 constexpr int LWIN = 2 * LJ - 1;                    // most recent terms per dot
 constexpr int NBLK = (2 * TB - 1 + LJ - 1) / LJ;    // blocks covering the sweep
 constexpr int NSTEP = NBLK * LJ;                    // steps including the idle tail
-constexpr int LEAF_THREADS = 768;                   // 12 waves, three per SIMD
-constexpr int NHELP = 576;                          // helper lanes: every wave not on SIMD 0
-static_assert(NHELP / 64 == 9 && 16 * 8 == 2 * TB, "nine helper waves cover 8 blocks of 16 units");
-// wave 0 is the chain; waves 4 and 8 (on the chain's SIMD) only take part in
-// the barriers, so the chain has its SIMD to itself
+constexpr int LEAF_THREADS = 768;                   // 12 waves, three per SIMD (wave w on SIMD w % 4)
+static_assert(16 * 8 == 2 * TB, "at most 8 blocks of 16 helper units");
 constexpr int WSP = NSTEP + 4;                      // row stride of the skewed W copy
 constexpr int CX = TB;                              // index of column 0 in the padded LA tables
 constexpr int NCX = CX + NSTEP + 4;                 // padded LA table length (columns -64 .. 131)
@@ -491,14 +488,16 @@ __device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float
     *dst = tot;
 }
 
-// helper waves: hw = 0..8 (SIMD 1 + hw % 3), lane groups of 4.  Units are
-// taken in order of decreasing length, 16 to a wave; the blocks of 16 are
-// dealt to the waves in a snake over the three SIMDs (longest to the first
-// wave of each SIMD, then back), so every SIMD gets a similar share.
-__device__ __forceinline__ void leaf_helpers(const int hw, const int lane) {
-    constexpr int kBlockOf[9] = {0, 1, 2, 5, 4, 3, 6, 7, 8};
+// helper waves w = 1..11, lane groups of 4.  Units are taken in order of
+// decreasing length, 16 to a wave (at most 8 such blocks).  The six longest
+// blocks go in pairs to SIMDs 1-3 (blocks 0 + 5, 1 + 4, 2 + 3: equal chunk
+// counts when all 8 are in use), the two shortest to the waves that share
+// the chain's SIMD (4 and 8), which otherwise idle; waves 9-11 get none.
+// The chain's instruction rate is unchanged by them (measured).
+__device__ __forceinline__ void leaf_helpers(const int w, const int lane) {
+    constexpr int kBlockOf[12] = {-1, 0, 1, 2, 6, 5, 4, 3, 7, 8, 8, 8};
     const int q = lane & 3;
-    const int g = 16 * kBlockOf[hw] + (lane >> 2);  // this group's unit rank
+    const int g = 16 * kBlockOf[w] + (lane >> 2);  // this group's unit rank (>= 128: none)
     for (int t = 0; t < NBLK; ++t) {
         if (t + 1 < NBLK) {
             // bulk of block t+1: diagonals D0 .. D0+LJ-1, terms of steps < s0
@@ -600,11 +599,6 @@ __device__ __forceinline__ void leaf_push(const LeafArgs &a, int I, int J, int w
     }
 }
 
-// the waves that share the chain's SIMD: barriers only
-__device__ __forceinline__ void leaf_idle() {
-    for (int t = 0; t < NBLK; ++t) __syncthreads();
-}
-
 // flags: LEAF_PULL subtract the contributions pushed by the previous leaf;
 // LEAF_PUSH compute this tile's contributions to the next tile diagonal
 constexpr int LEAF_PULL = 1, LEAF_PUSH = 2;
@@ -671,8 +665,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (w == 0) leaf_chain<ZP>(tid, (float)a.qmin, (float)a.qmax);
-    else if ((w & 3) == 0) leaf_idle();
-    else leaf_helpers(w - 1 - (w >> 2), tid & 63);
+    else leaf_helpers(w, tid & 63);
     const float *Es = lf_E;
     const float4 *s_row = lf_row;
 
