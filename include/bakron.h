@@ -193,9 +193,9 @@ int32_t bakron_quantize_antidiag(const float *W, int64_t m, int64_t n, const flo
  *   9 recursion depth (levels)
  *  10 useful flops of the band GEMM launches: out[6] without the zero half of
  *     the triangular diagonal factor blocks
- *  11 flops of the leaf pulls: a recursion node over two tile diagonals has no
- *     launch of its own; the leaf of its second diagonal applies its update
- *     (up to four dense b x b x b products per tile)
+ *  11 flops of the two-diagonal nodes: a recursion node over two tile
+ *     diagonals has no launch of its own; its update (up to four dense
+ *     b x b x b products per tile) runs inside the leaves of its two diagonals
  *  12 leaf launches that pull
  *  13 of the band launches in out[2]: deferred ones (side stream)
  *  14 useful flops of the deferred launches (part of out[10])

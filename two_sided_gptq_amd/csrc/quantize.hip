@@ -290,7 +290,9 @@ __shared__ __align__(32) float lf_ila[NCX];      // CX + c: 1 / LA_cc; 0 off 0..
 __shared__ float4 lf_row[TB];                    // (s, 1/s, z, 1/LB_rr)
 __shared__ __align__(32) float lf_bulk[2 * 2 * TB * LJ];  // [buffer][direction][row][step in block]
 __shared__ float lf_sink[3 * TB];                // write targets of idle lanes
-__shared__ __align__(16) float lf_P[2 * TB * GP]; // push operands: LA(J+1,J), then LB(I+1,I)
+__shared__ __align__(16) float lf_P[2 * TB * GP]; // push operands: LA(J+1,J), then LB(I+1,I);
+                                                  // a pulling leaf: the pushed V, skewed like W
+static_assert(TB * WSP <= 2 * TB * GP, "the skewed V fits the push operands' area");
 
 // the value lane l-1 holds, in lane l (lane 0 gets 0): a whole-wave shift
 __device__ __forceinline__ float from_lane_above(float x) {
@@ -305,13 +307,16 @@ __device__ __forceinline__ int clamp_col(int c) { return min(max(c, 0), TB - 1);
 // operands of block t+1 are loaded while block t runs.
 struct ChainBlock {
     float4 w4;           // W[r][d - r] for the block's LJ steps
+    float4 v4;           // pulling leaf: V[r][d - r] for the block's LJ steps
     float4 a[LJ][2];     // LA band of each step's column
     float ila[LJ];       // 1 / LA_cc of each step's column
 };
 
+template <bool PV>
 __device__ __forceinline__ void chain_load(ChainBlock &cb, const float *wrow, const float4 *ab,
                                            const float *ib, int t) {
     cb.w4 = *reinterpret_cast<const float4 *>(wrow + LJ * t);
+    if (PV) cb.v4 = *reinterpret_cast<const float4 *>(wrow - lf_Wk + lf_P + LJ * t);
 #pragma unroll
     for (int p = 0; p < LJ; ++p) {
         const int d = LJ * t + p;
@@ -332,8 +337,9 @@ struct ChainState {
 
 // Block t: the bulk of its steps is read first (it is the only operand the
 // helpers wrote during the previous block), then the next block's constant
-// operands are requested, then the LJ steps run.
-template <bool ZP>
+// operands are requested, then the LJ steps run.  PV: the leaf pulls V, which
+// starts each entry's row-direction sum.
+template <bool ZP, bool PV>
 __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb, ChainBlock &next,
                                             const float *wrow, const float4 *ab, const float *ib,
                                             int t) {
@@ -344,8 +350,9 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
         bulk1[p] = lf_bulk[(((t & 1) * 2 + 0) * TB + r) * LJ + p];
         bulk2[p] = lf_bulk[(((t & 1) * 2 + 1) * TB + r) * LJ + p];
     }
-    chain_load(next, wrow, ab, ib, t + 1);
+    chain_load<PV>(next, wrow, ab, ib, t + 1);
     const float wv[4] = {cb.w4.x, cb.w4.y, cb.w4.z, cb.w4.w};
+    const float vv[4] = {cb.v4.x, cb.v4.y, cb.v4.z, cb.v4.w};
 #pragma unroll
     for (int p = 0; p < LJ; ++p) {
         const int d = LJ * t + p;
@@ -353,7 +360,7 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
                              cb.a[p][1].x, cb.a[p][1].y, cb.a[p][1].z, cb.a[p][1].w};
         // the bulk, then the recent terms j = LJ + p .. 2 (steps s0 .. d-2),
         // then the fresh j = 1
-        float y = bulk1[p], s2 = bulk2[p];
+        float y = PV ? bulk1[p] + vv[p] : bulk1[p], s2 = bulk2[p];
 #pragma unroll
         for (int j = LJ + p; j >= 2; --j) {
             y = fmaf(st.eh[j - 1], la[j], y);
@@ -391,7 +398,7 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
     *reinterpret_cast<float4 *>(st.wrow + LJ * t) = make_float4(code[0], code[1], code[2], code[3]);
 }
 
-template <bool ZP>
+template <bool ZP, bool PV>
 __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const float qmaxf) {
     __builtin_assume(r >= 0 && r < TB);
     ChainState st;
@@ -410,11 +417,11 @@ __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const
     const float4 *ab = lf_Ab + 2 * (CX - r);  // step d: ab[2d], ab[2d + 1]
     const float *ib = lf_ila + (CX - r);      // step d: ib[d]
     ChainBlock c0, c1;
-    chain_load(c0, st.wrow, ab, ib, 0);
+    chain_load<PV>(c0, st.wrow, ab, ib, 0);
     for (int t = 0; t < NBLK; t += 2) {
-        chain_block<ZP>(st, c0, c1, st.wrow, ab, ib, t);
+        chain_block<ZP, PV>(st, c0, c1, st.wrow, ab, ib, t);
         __syncthreads();
-        chain_block<ZP>(st, c1, c0, st.wrow, ab, ib, t + 1);
+        chain_block<ZP, PV>(st, c1, c0, st.wrow, ab, ib, t + 1);
         __syncthreads();
     }
 }
@@ -520,16 +527,22 @@ __device__ __forceinline__ void leaf_helpers(const int w, const int lane) {
 // A recursion node over two tile diagonals [K, K+2) has a band update from
 // diagonal K to K+1 alone.  It gets no launch: the leaf of diagonal K, which
 // holds E(I,J), LA(J,J) and LB(I,I) in LDS and has prefetched LA(J+1,J) and
-// LB(I+1,I), computes the two contributions of its tile,
-//   to (I+1, J):  LB(I+1,I) (E(I,J) LA(J,J)^T)
-//   to (I, J+1):  LB(I,I) (E(I,J) LA(J+1,J)^T),
-// into the workspace, and the leaf of diagonal K+1 subtracts them while it
-// loads its W tile.  E(I,J) LA(J,J)^T is the sweep's Z (each step forms
-// z = E[r][c] LA[c][c] + sum_{k<c} E[r][k] LA[c][k]), which lf_Z already holds
-// transposed; the other three products run on fp32 MFMA in 32 x 32 quadrants
-// (waves 0-3, one per SIMD); lane l supplies row l % 32 of both operands and
-// the k half l / 32; the triangular diagonal blocks cut the k range of the
-// quadrants that allow it.
+// LB(I+1,I), writes what its tile contributes to the next tile diagonal
+// into the workspace:
+//   Cd, to (I+1, J):  LB(I+1,I) U, U = E(I,J) LA(J,J)^T,
+//   Cr, to (I, J+1):  V = E(I,J) LA(J+1,J)^T,
+// and the leaf of diagonal K+1 applies them:
+//   it subtracts Cd from its W tile as it loads it;
+//   it applies LB(I,I) to V inside its own sweep: with V[r][c] added to the
+//   row-direction sum of entry (r, c), that entry's z carries V[r][c] too,
+//   so the column-direction sums subtract sum_{k<r} LB[r][k] V[k][c] and the
+//   row term LB[r][r] V[r][c] -- together (LB(I,I) V)[r][c].
+// U is the sweep's Z (each step forms z = E[r][c] LA[c][c] +
+// sum_{k<c} E[r][k] LA[c][k]), which lf_Z already holds transposed, so two
+// products remain.  They run on fp32 MFMA in 32 x 32 quadrants (waves 0-3,
+// one per SIMD; lane l supplies row l % 32 of both operands and the k half
+// l / 32), right after the sweep and beside the other waves' epilogue: they
+// only read LDS that is final once the sweep has ended.
 
 // acc += A[i][k] B[j][k]^T over k < KN for the 32 x 32 block; fa(i, k), fb(j, k)
 // return the float4 at k .. k+3 of row i (j) of the block.
@@ -551,56 +564,39 @@ __device__ __forceinline__ float4 lds4(const float *base, int stride, int row, i
     return *reinterpret_cast<const float4 *>(base + row * stride + k);
 }
 
-// waves 0-3: quadrant (w >> 1, w & 1).  Phase 1 stores V^T (stride GP) in
-// the skewed-W area, free once the sweep's outputs are written; phase 2 writes
-// the contributions (U^T is the sweep's Z^T in lf_Z, stride LP).
-__device__ __forceinline__ void leaf_push(const LeafArgs &a, int I, int J, int w, bool phase2) {
+// waves 0-3: quadrant (w >> 1, w & 1) of both contributions
+__device__ __forceinline__ void leaf_push(const LeafArgs &a, int I, int J, int w) {
     const int lane = threadIdx.x & 63;
     const int qr = w >> 1, qc = w & 1;
     const bool down = I + 1 < a.M, right = J + 1 < a.N;
     const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
     const int rb = 32 * qr, cb = 32 * qc;
-    const float *Ut = lf_Z;
-    float *Vt = lf_Wk;
     floatx16 acc, acc2;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = acc2[v] = 0.0f;
-    if (!phase2) {
-        if (!right) return;
-        {  // V = E LA(J+1,J)^T
-            auto fa = [&](int i, int k) { return lds4(lf_E, LP, rb + i, k); };
-            auto fb = [&](int j, int k) { return lds4(lf_P, GP, cb + j, k); };
-            mfma_block<64>(acc2, fa, fb);
-        }
-        // accumulator: lane holds column lane % 32, register v row 8(v/4) + 4(lane/32) + v%4
+    if (down) {  // LB(I+1,I) U with U^T = Z^T
+        auto fa = [&](int i, int k) { return lds4(lf_P + TB * GP, GP, rb + i, k); };
+        auto fb = [&](int j, int k) { return lds4(lf_Z, LP, cb + j, k); };
+        mfma_block<64>(acc, fa, fb);
+    }
+    if (right) {  // V = E LA(J+1,J)^T
+        auto fa = [&](int i, int k) { return lds4(lf_E, LP, rb + i, k); };
+        auto fb = [&](int j, int k) { return lds4(lf_P, GP, cb + j, k); };
+        mfma_block<64>(acc2, fa, fb);
+    }
+    // accumulator: lane holds column lane % 32, register v row 8(v/4) + 4(lane/32) + v%4
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rr = rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cc = cb + (lane & 31);
-            Vt[cc * GP + rr] = acc2[v];
-        }
-    } else {
-        if (down) {  // LB(I+1,I) U with U^T = Z^T
-            auto fa = [&](int i, int k) { return lds4(lf_P + TB * GP, GP, rb + i, k); };
-            auto fb = [&](int j, int k) { return lds4(Ut, LP, cb + j, k); };
-            mfma_block<64>(acc, fa, fb);
-        }
-        if (right) {  // LB(I,I) V
-            auto fa = [&](int i, int k) { return lds4(lf_B, LP, rb + i, k); };
-            auto fb = [&](int j, int k) { return lds4(Vt, GP, cb + j, k); };
-            if (qr) mfma_block<64>(acc2, fa, fb);
-            else mfma_block<32>(acc2, fa, fb);
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t rr = rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cc = cb + (lane & 31);
-            if (down) a.Cd[(r0 + TB + rr) * a.np + c0 + cc] = acc[v];
-            if (right) a.Cr[(r0 + rr) * a.np + c0 + TB + cc] = acc2[v];
-        }
+    for (int v = 0; v < 16; ++v) {
+        const int64_t rr = rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), cc = cb + (lane & 31);
+        if (down) a.Cd[(r0 + TB + rr) * a.np + c0 + cc] = acc[v];
+        if (right) a.Cr[(r0 + rr) * a.np + c0 + TB + cc] = acc2[v];
     }
 }
 
-// flags: LEAF_PULL subtract the contributions pushed by the previous leaf;
-// LEAF_PUSH compute this tile's contributions to the next tile diagonal
+// flags: LEAF_PULL apply the contributions pushed by the previous leaf;
+// LEAF_PUSH compute this tile's contributions to the next tile diagonal.
+// A leaf has at most one of them: a pulling leaf keeps the pushed V in the
+// push operands' LDS (lf_P), which it does not otherwise use.
 constexpr int LEAF_PULL = 1, LEAF_PUSH = 2;
 
 template <bool ZP>
@@ -620,9 +616,13 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
             const float4 d = *reinterpret_cast<const float4 *>(a.Cd + g);
             wv.x -= d.x; wv.y -= d.y; wv.z -= d.z; wv.w -= d.w;
         }
-        if (pull_left) {
-            const float4 d = *reinterpret_cast<const float4 *>(a.Cr + g);
-            wv.x -= d.x; wv.y -= d.y; wv.z -= d.z; wv.w -= d.w;
+        if (pull_left) {  // V, applied in the sweep; stored skewed like W
+            const float4 v = *reinterpret_cast<const float4 *>(a.Cr + g);
+            float *vk = lf_P + r * WSP + r + c4;
+            vk[0] = v.x;
+            vk[1] = v.y;
+            vk[2] = v.z;
+            vk[3] = v.w;
         }
         float *wk = lf_Wk + r * WSP + r + c4;
         wk[0] = wv.x;
@@ -647,6 +647,12 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     }
     for (int idx = tid; idx < 2 * 2 * TB * LJ / 4; idx += LEAF_THREADS)
         reinterpret_cast<float4 *>(lf_bulk)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (pull_left) {  // the skewed V's slots outside a row's 64 entries
+        for (int idx = tid; idx < TB * (WSP - TB); idx += LEAF_THREADS) {
+            const int r = idx / (WSP - TB), k = idx - r * (WSP - TB);
+            lf_P[r * WSP + (k < r ? k : k + TB)] = 0.0f;
+        }
+    }
     __syncthreads();
     if (tid < TB) {
         const float s = a.sc[r0 + tid];
@@ -664,73 +670,77 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     __syncthreads();
 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (w == 0) leaf_chain<ZP>(tid, (float)a.qmin, (float)a.qmax);
+    if (w == 0) {
+        if (pull_left) leaf_chain<ZP, true>(tid, (float)a.qmin, (float)a.qmax);
+        else leaf_chain<ZP, false>(tid, (float)a.qmin, (float)a.qmax);
+    }
     else leaf_helpers(w, tid & 63);
-    const float *Es = lf_E;
-    const float4 *s_row = lf_row;
+    // waves 0-3 push (when the node asks for it) while the others write the
+    // outputs; both only read LDS that the sweep has finalised
+    const bool push = flags & LEAF_PUSH;
+    if (push && w < 4) leaf_push(a, I, J, w);
+    const int et = push ? tid - 4 * 64 : tid, en = push ? LEAF_THREADS - 4 * 64 : LEAF_THREADS;
+    if (et >= 0) {
+        const float *Es = lf_E;
+        const float4 *s_row = lf_row;
 
-    // E tile to the band-update buffer
-    if (a.order == BAKRON_ORDER_LA_FIRST) {
-        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
-            const int r = idx >> 4, c4 = (idx & 15) * 4;
-            *reinterpret_cast<float4 *>(a.Ebuf + (r0 + r) * a.np + c0 + c4) =
-                *reinterpret_cast<const float4 *>(Es + r * LP + c4);
-        }
-    } else {
-        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
-            const int c = idx >> 4, rr4 = (idx & 15) * 4;
-            *reinterpret_cast<float4 *>(a.Ebuf + (c0 + c) * a.mp + r0 + rr4) =
-                make_float4(Es[(rr4 + 0) * LP + c], Es[(rr4 + 1) * LP + c],
-                            Es[(rr4 + 2) * LP + c], Es[(rr4 + 3) * LP + c]);
-        }
-    }
-    // caller-visible outputs
-    int bad = 0;
-    if (a.out_vec) {
-        // groups of 4 columns: with ldo % 4 == 0 (and so n % 4 == 0) a group is
-        // wholly inside or outside
-        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
-            const int r = idx >> 4, c4 = (idx & 15) * 4;
-            const int64_t gi = r0 + r, gj = c0 + c4;
-            const float4 e = *reinterpret_cast<const float4 *>(Es + r * LP + c4);
-            bad |= (!isfinite(e.x) || !isfinite(e.y) || !isfinite(e.z) || !isfinite(e.w));
-            if (gi < a.m && gj < a.n) {
-                const float *wk = lf_Wk + r * WSP + r + c4;
-                const float q0 = wk[0], q1 = wk[1], q2 = wk[2], q3 = wk[3];
-                const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q0) |
-                                        ((uint32_t)(uint8_t)(int8_t)(int)q1 << 8) |
-                                        ((uint32_t)(uint8_t)(int8_t)(int)q2 << 16) |
-                                        ((uint32_t)(uint8_t)(int8_t)(int)q3 << 24);
-                *reinterpret_cast<uint32_t *>(a.codes + gi * a.ldo + gj) = packed;
-                const float4 rc = s_row[r];
-                if (a.V)
-                    *reinterpret_cast<float4 *>(a.V + gi * a.ldo + gj) =
-                        make_float4(rc.x * (q0 - rc.z), rc.x * (q1 - rc.z), rc.x * (q2 - rc.z),
-                                    rc.x * (q3 - rc.z));
-                if (a.E) *reinterpret_cast<float4 *>(a.E + gi * a.ldo + gj) = e;
+        // E tile to the band-update buffer
+        if (a.order == BAKRON_ORDER_LA_FIRST) {
+            for (int idx = et; idx < TB * 16; idx += en) {
+                const int r = idx >> 4, c4 = (idx & 15) * 4;
+                *reinterpret_cast<float4 *>(a.Ebuf + (r0 + r) * a.np + c0 + c4) =
+                    *reinterpret_cast<const float4 *>(Es + r * LP + c4);
+            }
+        } else {
+            for (int idx = et; idx < TB * 16; idx += en) {
+                const int c = idx >> 4, rr4 = (idx & 15) * 4;
+                *reinterpret_cast<float4 *>(a.Ebuf + (c0 + c) * a.mp + r0 + rr4) =
+                    make_float4(Es[(rr4 + 0) * LP + c], Es[(rr4 + 1) * LP + c],
+                                Es[(rr4 + 2) * LP + c], Es[(rr4 + 3) * LP + c]);
             }
         }
-    } else {
-        for (int idx = tid; idx < TB * TB; idx += LEAF_THREADS) {
-            const int r = idx >> 6, c = idx & 63;
-            const int64_t gi = r0 + r, gj = c0 + c;
-            bad |= !isfinite(Es[r * LP + c]);
-            if (gi < a.m && gj < a.n) {
-                const float qf = lf_Wk[r * WSP + r + c];
-                const int8_t code = (int8_t)(int)qf;
-                a.codes[gi * a.ldo + gj] = code;
-                const float4 rc = s_row[r];
-                if (a.V) a.V[gi * a.ldo + gj] = rc.x * (qf - rc.z);
-                if (a.E) a.E[gi * a.ldo + gj] = Es[r * LP + c];
+        // caller-visible outputs
+        int bad = 0;
+        if (a.out_vec) {
+            // groups of 4 columns: with ldo % 4 == 0 (and so n % 4 == 0) a group is
+            // wholly inside or outside
+            for (int idx = et; idx < TB * 16; idx += en) {
+                const int r = idx >> 4, c4 = (idx & 15) * 4;
+                const int64_t gi = r0 + r, gj = c0 + c4;
+                const float4 e = *reinterpret_cast<const float4 *>(Es + r * LP + c4);
+                bad |= (!isfinite(e.x) || !isfinite(e.y) || !isfinite(e.z) || !isfinite(e.w));
+                if (gi < a.m && gj < a.n) {
+                    const float *wk = lf_Wk + r * WSP + r + c4;
+                    const float q0 = wk[0], q1 = wk[1], q2 = wk[2], q3 = wk[3];
+                    const uint32_t packed = ((uint32_t)(uint8_t)(int8_t)(int)q0) |
+                                            ((uint32_t)(uint8_t)(int8_t)(int)q1 << 8) |
+                                            ((uint32_t)(uint8_t)(int8_t)(int)q2 << 16) |
+                                            ((uint32_t)(uint8_t)(int8_t)(int)q3 << 24);
+                    *reinterpret_cast<uint32_t *>(a.codes + gi * a.ldo + gj) = packed;
+                    const float4 rc = s_row[r];
+                    if (a.V)
+                        *reinterpret_cast<float4 *>(a.V + gi * a.ldo + gj) =
+                            make_float4(rc.x * (q0 - rc.z), rc.x * (q1 - rc.z), rc.x * (q2 - rc.z),
+                                        rc.x * (q3 - rc.z));
+                    if (a.E) *reinterpret_cast<float4 *>(a.E + gi * a.ldo + gj) = e;
+                }
+            }
+        } else {
+            for (int idx = et; idx < TB * TB; idx += en) {
+                const int r = idx >> 6, c = idx & 63;
+                const int64_t gi = r0 + r, gj = c0 + c;
+                bad |= !isfinite(Es[r * LP + c]);
+                if (gi < a.m && gj < a.n) {
+                    const float qf = lf_Wk[r * WSP + r + c];
+                    const int8_t code = (int8_t)(int)qf;
+                    a.codes[gi * a.ldo + gj] = code;
+                    const float4 rc = s_row[r];
+                    if (a.V) a.V[gi * a.ldo + gj] = rc.x * (qf - rc.z);
+                    if (a.E) a.E[gi * a.ldo + gj] = Es[r * LP + c];
+                }
             }
         }
-    }
-    if (bad && a.dev_status) atomicOr(a.dev_status, BAKRON_DEV_NONFINITE);
-    if (flags & LEAF_PUSH) {
-        __syncthreads();  // the skewed-W area (codes) has been read
-        if (w < 4) leaf_push(a, I, J, w, false);
-        __syncthreads();
-        if (w < 4) leaf_push(a, I, J, w, true);
+        if (bad && a.dev_status) atomicOr(a.dev_status, BAKRON_DEV_NONFINITE);
     }
 }
 
@@ -1359,8 +1369,9 @@ BandCount band_flops(const Plan &pl, int order, int M, int N) {
     return c;
 }
 
-// Two-diagonal nodes: every leaf that pushes runs up to two products per
-// target tile (dense 64 x 64 x 64 fp32 MFMA).
+// Two-diagonal nodes: the update of each target tile is two dense
+// 64 x 64 x 64 products (LB E LA^T); the leaves run them as one MFMA product
+// each (U comes from the sweep, and LB(I,I) V is applied inside the next sweep).
 void pull_counts(int M, int N, double *flops, int *leaves) {
     std::vector<Node> nodes;
     build_nodes(0, M + N - 1, nodes);
