@@ -8,12 +8,16 @@ resident in HBM before timing; LA and LB come from bakron_hessian and
 bakron_factor on the synthetic samples (untimed preparation).
 
 Prints one JSON line.  Besides the contract fields it carries
-  roofline      for the dominant kernel (band GEMM: fp32 MFMA peak), with
-                algorithmic flops / average launch duration from HIP events
-                recorded inside the library on the solver's stream, and the
-                MFMA utilisation from the committed counter summary (fp32
-                MFMA flops counted per dispatch over that same duration)
-  leaf          the leaf phase: HBM bytes per launch, launches, in-kernel steps
+  roofline      for the band GEMM (fp32 MFMA peak), the kernel the metric's
+                "% of fp32 MFMA peak" names, with algorithmic flops / average
+                launch duration from HIP events recorded inside the library on
+                the solver's stream, and the MFMA utilisation from the committed
+                counter summary (fp32 MFMA flops counted per dispatch over that
+                same duration).  The leaf kernel takes about as long in total
+                (dominant_kernel names the longer phase) but is bound by its
+                chain of dependent steps, not by a throughput roofline
+  leaf          the leaf phase: HBM bytes per launch, launches, in-kernel steps,
+                and its in-tile flops against the fp32 vector peak
   cpu_baseline  the fp64 oracle (BaKron-naive) on a bounded leading block of
                 the same problem, on this host's cores
 """
@@ -31,6 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP32_MFMA_PEAK_TFLOPS = 157.3
+# MI355X's published fp32 vector peak; it counts packed two-wide fp32 FMAs,
+# which this library's kernels do not use (scalar FMAs reach half of it)
+FP32_VALU_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 PROFILE_MD = os.path.join(ROOT, "profiles", "band_gemm_leaf_4096x4096_int4.md")
 
@@ -207,6 +214,9 @@ def main():
                  "useful_flops": sched["side_useful_flops"],
                  "replay_ms": ph["side_replay_ms"], "tflops_alone": side_tflops},
         "leaf": {"launches": int(sched["leaf_launches"]), "in_kernel_steps": int(sched["leaf_steps"]),
+                 "in_tile_flops": sched["leaf_flops"],
+                 "valu_tflops": sched["leaf_flops"] / (ph["leaf_ms"] / 1e3) / 1e12,
+                 "valu_frac": sched["leaf_flops"] / (ph["leaf_ms"] / 1e3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
                  "avg_launch_ms": leaf_avg_s * 1e3, "alg_bytes": leaf_bytes,
                  "achieved_GBs": leaf_gbs, "hbm_frac": leaf_gbs / HBM_PEAK_GBS},
         "schedule": sched,
