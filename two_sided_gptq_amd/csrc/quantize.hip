@@ -888,10 +888,10 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
 }
 
 // Band products that run beside the leaves.  A launch has at most SIDE_WG
-// workgroups of 1024 threads, and each workgroup's LDS (four tiles' operand
-// blocks, 139 KB) keeps it alone on its CU, so a side launch never holds more
-// than SIDE_WG CUs: the leaves, one workgroup of 160 KB LDS per tile, always
-// find empty CUs.  The four 4-wave slots of a workgroup work independently,
+// (or SIDE_WG_QUARTER) workgroups of 1024 threads, and each workgroup's LDS
+// (four tiles' operand blocks, 139 KB) keeps it alone on its CU, so a side
+// launch leaves at least 64 CUs to the leaves (one workgroup of 160 KB LDS
+// per tile; a tile diagonal of up to 64 tiles finds them empty).  The four 4-wave slots of a workgroup work independently,
 // like four workgroups of band_gemm_kernel.  The launch's tiles, in
 // band_gemm_kernel's grid order (row-major, longest first), go first to slot 0
 // of every workgroup, then slot 1, and so on (one tile per CU before two);
@@ -903,6 +903,11 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
 // is bounded all the same, and a wait that reaches the bound sets
 // BAKRON_DEV_SPIN_LIMIT in *dev_status.
 constexpr int SIDE_WG = 160;
+// Shapes whose plan keeps a quarter of each wide node critical defer less per
+// leaf; their side launches take more CUs (measured at 4096 x 4096: 160 ->
+// 6.23 ms, 176 -> 6.19, 192 -> 6.18, 208 -> 6.28).  Shapes that keep half
+// stay at SIDE_WG (11008 x 4096: 17.8 ms with 160, 18.0 with 192).
+constexpr int SIDE_WG_QUARTER = 192;
 constexpr int SIDE_THREADS = 1024;
 constexpr int SPIN_LIMIT = 1 << 22;
 
@@ -1438,6 +1443,7 @@ struct ShapeInfo {
     int auto_order;
     Plan plan;
     int side_ops;     // deferred products of the plan (one tile counter each)
+    int side_wg;      // workgroups of a side launch
 };
 
 std::mutex g_shape_mu;
@@ -1450,6 +1456,7 @@ const ShapeInfo &shape_info(int M, int N) {
     if (it != g_shapes.end()) return it->second;
     ShapeInfo s{};
     for (int shift = 2; shift >= 1; --shift) {
+        s.side_wg = shift == 2 ? SIDE_WG_QUARTER : SIDE_WG;
         s.plan = build_plan(M, N, shift);
         s.band[1] = band_flops(s.plan, BAKRON_ORDER_LA_FIRST, M, N);
         s.band[2] = band_flops(s.plan, BAKRON_ORDER_LB_FIRST, M, N);
@@ -1943,7 +1950,7 @@ int32_t launch_band(const Solve &sv, const Op &op, int *ctr, hipStream_t stream,
     }
     if (op.side) {
         // one workgroup per CU, up to one per tile
-        const int wgs = std::min(SIDE_WG, cols * rows);
+        const int wgs = std::min(shape_info(sv.M, sv.N).side_wg, cols * rows);
         hipLaunchKernelGGL(band_side_kernel, dim3(wgs), dim3(SIDE_THREADS), 0, stream, g, ctr,
                            sv.dev_status);
         BK_LAUNCH_CHECK("band_side_kernel");
