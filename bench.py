@@ -40,6 +40,7 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 FP32_VALU_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 PROFILE_MD = os.path.join(ROOT, "profiles", "band_gemm_leaf_4096x4096_int4.md")
+PROFILED_WORKLOAD = "c3"  # the workload and launch configuration the summary was taken on
 
 
 def parse():
@@ -159,14 +160,15 @@ def main():
     # the timing call's replay of the critical band launches alone, as a graph
     # whose kernels start back to back, between two HIP events on the stream
     band_launches = ph["band_launches"]
-    gemm_avg_s = ph["band_replay_ms"] / 1e3 / band_launches
+    # a single tile diagonal (64 x 64) has no band launch: the band figures are null
+    gemm_avg_s = ph["band_replay_ms"] / 1e3 / band_launches if band_launches else None
     # algorithmic flops of the band-GEMM launches: the useful multiply-adds of
     # their tiles (the zero halves of triangular diagonal factor blocks left
     # out); the two-diagonal nodes run inside the leaves and are not counted
     crit_useful = sched["useful_band_flops"] - sched["side_useful_flops"]
     assert band_launches == sched["band_launches"] - sched["side_launches"]
-    gemm_alg_per_launch = crit_useful / band_launches
-    gemm_tflops = gemm_alg_per_launch / gemm_avg_s / 1e12
+    gemm_alg_per_launch = crit_useful / band_launches if band_launches else None
+    gemm_tflops = gemm_alg_per_launch / gemm_avg_s / 1e12 if band_launches else None
     side_tflops = (sched["side_useful_flops"] / (ph["side_replay_ms"] / 1e3) / 1e12
                    if ph["side_launches"] else None)
     leaf_avg_s = ph["leaf_ms"] / 1e3 / sched["leaf_launches"]
@@ -176,18 +178,22 @@ def main():
     leaf_gbs = leaf_bytes / sched["leaf_launches"] / leaf_avg_s / 1e9
     dominant = "band_gemm" if ph["band_ms"] >= ph["leaf_ms"] else "leaf"
     # HBM bytes per band-GEMM dispatch from the committed rocprofv3 counter
-    # summary, null unless it was taken from the current kernel source
+    # summary of the 4096 x 4096 workload (this default run), null for other
+    # workloads and unless it was taken from the current kernel source
     from two_sided_gptq_amd import profsum
-    traffic = profsum.read_traffic(PROFILE_MD, "band_gemm_kernel")
+    profiled = args.workload == PROFILED_WORKLOAD and args.order == 0 and not args.eager
+    traffic = profsum.read_traffic(PROFILE_MD, "band_gemm_kernel") if profiled else None
     # MFMA utilisation from the same summary's counters: fp32 MFMA flops the
     # hardware counted per dispatch (executed, so the zero halves of triangular
     # blocks included) over this run's average launch duration, against the peak
-    counted = profsum.read_figure(PROFILE_MD, "mfma_flops_per_dispatch", "band_gemm_kernel")
-    mfma_util = counted / gemm_avg_s / 1e12 / FP32_MFMA_PEAK_TFLOPS if counted else None
+    counted = (profsum.read_figure(PROFILE_MD, "mfma_flops_per_dispatch", "band_gemm_kernel")
+               if profiled else None)
+    mfma_util = counted / gemm_avg_s / 1e12 / FP32_MFMA_PEAK_TFLOPS if counted and gemm_avg_s else None
     roofline = {"kernel": "band_gemm_kernel", "bound": "mfma", "achieved": gemm_tflops,
                 "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": gemm_tflops / FP32_MFMA_PEAK_TFLOPS, "traffic": traffic,
-                "alg_flops_per_launch": gemm_alg_per_launch, "avg_launch_ms": gemm_avg_s * 1e3,
+                "frac": gemm_tflops / FP32_MFMA_PEAK_TFLOPS if gemm_tflops else None,
+                "traffic": traffic, "alg_flops_per_launch": gemm_alg_per_launch,
+                "avg_launch_ms": gemm_avg_s * 1e3 if gemm_avg_s else None,
                 "launches": band_launches, "counted_mfma_flops_per_launch": counted,
                 "mfma_util_counted": mfma_util}
 
@@ -204,7 +210,7 @@ def main():
                    "launch": "eager" if args.eager else "graph"},
         "roofline": roofline,
         "dominant_kernel": dominant,
-        "gemm_pct_fp32_mfma_peak": 100.0 * gemm_tflops / FP32_MFMA_PEAK_TFLOPS,
+        "gemm_pct_fp32_mfma_peak": 100.0 * gemm_tflops / FP32_MFMA_PEAK_TFLOPS if gemm_tflops else None,
         "whole_solve_tflops_alg": sched["alg_band_flops"] / (ms / 1e3) / 1e12,
         # phase times come from a separate timing pass that runs the same plan in
         # order on one stream; the timed graph overlaps the deferred products

@@ -51,3 +51,16 @@ def test_report_fields():
         assert k in cb, k
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert "48x48" in cb["sample"]
+
+
+@pytest.mark.gpu
+def test_report_single_tile_workload():
+    # 64 x 64 is one tile diagonal: no band launch, so the band figures are null
+    # (and counters from the 4096 x 4096 profile are not attached to it)
+    p = _run(["--workload", "c1", "--steps", "2", "--warmup", "1", "--cpu-sample", "16"], 300)
+    assert p.returncode == 0, p.stderr[-2000:]
+    r = json.loads([l for l in p.stdout.strip().splitlines() if l.startswith("{")][-1])
+    assert r["value"] > 0 and r["config"]["m"] == 64
+    assert r["roofline"]["achieved"] is None and r["roofline"]["frac"] is None
+    assert r["roofline"]["traffic"] is None
+    assert r["leaf"]["launches"] == 1
