@@ -209,29 +209,49 @@ def _round_np(P, s, z, qmin, qmax):
     return c, s * (c - z)
 
 
-def gptq_rows(W, LA, scales, zeros, kind, bits):
+def gptq_rows(W, LA, scales, zeros, kind, bits, ref_codes=None, window=1e-4):
     """Ordinary one-sided GPTQ (every row independent), Hessian A on the input
     side: for each column j, round, err = (w_j - q_j) / LA[j,j], and feed the
     error forward along the row through column j of LA.  (Load-bearing premise:
-    GPTQ is the case E[xx^T] (x) I, i.e. B = I.)"""
+    GPTQ is the case E[xx^T] (x) I, i.e. B = I.)
+
+    With ``ref_codes`` the boundary ties are settled as in ``naive``: an entry
+    whose pre-rounding value u = P / s lies within ``window`` code units of an
+    interior rounding boundary takes the reference code if that is one of the
+    two adjacent codes (counted in ``ties``); a tie whose reference is neither
+    neighbour, and any other disagreement, is counted in ``mismatches`` and the
+    oracle keeps its own code."""
     Wk = np.array(W, dtype=np.float64)
     LA = np.asarray(LA, dtype=np.float64)
     s = np.asarray(scales, dtype=np.float64)
     z = np.asarray(zeros, dtype=np.float64)
     qmin, qmax = qrange(kind, bits)
     m, n = Wk.shape
+    ref = None if ref_codes is None else np.asarray(ref_codes).astype(np.int64)
     codes = np.zeros((m, n), np.int32)
     V = np.zeros((m, n))
     E = np.zeros((m, n))
+    ties = mismatches = 0
     for j in range(n):
         P = Wk[:, j].copy()
         c, v = _round_np(P, s, z, qmin, qmax)
+        if ref is not None:
+            u = P / s
+            fl = np.floor(u)
+            lower = fl + z
+            tie = ((lower >= qmin) & (lower + 1 <= qmax) & (np.abs((u - fl) - 0.5) < window))
+            r = ref[:, j]
+            adopt = tie & ((r == lower) | (r == lower + 1))
+            ties += int(np.sum(adopt))
+            mismatches += int(np.sum(tie & ~adopt)) + int(np.sum(~tie & (r != c)))
+            c = np.where(adopt, r, c)
+            v = s * (c - z)
         err = (P - v) / LA[j, j]
         codes[:, j] = c
         V[:, j] = v
         E[:, j] = err
         Wk[:, j:] -= np.outer(err, LA[j:, j])
-    return dict(codes=codes, V=V, E=E)
+    return dict(codes=codes, V=V, E=E, ties=ties, mismatches=mismatches)
 
 
 def vec_gptq(W, A, B, scales, zeros, kind, bits):

@@ -147,6 +147,37 @@ def test_b_identity_is_rowwise_gptq_bitwise(m, n, kind, bits):
     assert np.array_equal(r["E"], g["E"])
 
 
+@pytest.mark.parametrize("kind,bits", [(SYM, 4), (ASYM, 2)])
+def test_b_identity_tie_adoption_matches_naive(kind, bits):
+    """Row GPTQ with tie adoption settles ties as the naive solver does at
+    B = I: with a wide window (many entries count as ties) and reference codes
+    that pick the other neighbour at every second tie, plus one reference code
+    that is no neighbour, both reach the same codes, values and counts."""
+    m, n = 12, 40
+    W, A, B, LA, LB, s, z = _problem(m, n, 907 + bits, kind=kind, bits=bits, b_identity=True)
+    window = 0.2
+    own = oracle.naive(W, LA, LB, s, z, kind, bits)
+    u = own["U"]
+    fl = np.floor(u)
+    qmin, qmax = oracle.qrange(kind, bits)
+    tie = (np.abs(u - fl - 0.5) < window) & (fl + z[:, None] >= qmin) & (fl + z[:, None] + 1 <= qmax)
+    assert np.sum(tie) > 20
+    ref = own["codes"].copy()
+    idx = np.argwhere(tie)[::2]
+    for i, j in idx:
+        lo = int(fl[i, j] + z[i])
+        ref[i, j] = lo if ref[i, j] == lo + 1 else lo + 1
+    ref[3, 7] = qmax if own["codes"][3, 7] < qmax - 2 else qmin
+    ref = ref.astype(np.int8)
+    r = oracle.naive(W, LA, LB, s, z, kind, bits, ref_codes=ref, window=window)
+    g = oracle.gptq_rows(W, LA, s, z, kind, bits, ref_codes=ref, window=window)
+    assert r["ties"] > 10 and r["mismatches"] >= 1
+    assert (g["ties"], g["mismatches"]) == (r["ties"], r["mismatches"])
+    assert np.array_equal(g["codes"], r["codes"])
+    assert np.array_equal(g["V"], r["V"]) and np.array_equal(g["E"], r["E"])
+    assert not np.array_equal(r["codes"], own["codes"])
+
+
 def test_a_identity_is_columnwise_gptq():
     """A = I: the problem is GPTQ down each column under B (the transposed
     problem), here on the unit grid so the per-row scale does not matter."""
