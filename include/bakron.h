@@ -152,8 +152,10 @@ int32_t bakron_factor(const float *H, int64_t d, float *L, int32_t *dev_status,
  * The schedule is captured once into an executable HIP graph, cached per
  * (device, sizes, quantizer, order, every pointer argument, ws) -- at most 16
  * graphs, least recently used dropped -- and replayed on `stream`.  The first
- * call with a new key pays the capture.  Not thread-safe across concurrent
- * calls that share a workspace (they race on it anyway).
+ * call with a new key pays the capture.  Calls from several host threads are
+ * safe when they use distinct workspaces and outputs: the cache is locked from
+ * lookup through launch, and an evicted graph is destroyed only after its
+ * last launch has completed.  Calls that share a workspace race on it.
  */
 size_t bakron_quantize_workspace_size(int64_t m, int64_t n, int32_t qkind, int32_t qbits);
 int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
@@ -213,7 +215,8 @@ int32_t bakron_schedule_info(int64_t m, int64_t n, int32_t flags, double *out);
  *   leaf:  [3] tile diagonal K, [4] 1 = applies the previous leaf's
  *          two-diagonal update, 2 = computes it for the next leaf
  *   band:  [3] K, [5] L, [6] H of the recursion node (split at K + H), [7] its
- *          depth (selects its T buffer), [8] product (0 first, 1 second),
+ *          T buffer (its recursion depth; the nodes below the deepest level
+ *          that defers products share one), [8] product (0 first, 1 second),
  *          [9..10] diagonal range lo, hi (T diagonals for the first product,
  *          W target diagonals for the second), then the launch grid for the
  *          order given in flags: [11] mode, [12] first band offset, [13] offsets,

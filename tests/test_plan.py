@@ -14,8 +14,8 @@ recorded before it).  Each step touches 64 x 64 tiles:
        mode 2 S(I', J) = sum_I LB(I', I) E(I, J)           (writes S, reads E)
        mode 3 W(I', J') -= sum_J S(I', J) LA(J', J)^T      (reads S, updates W)
 with the staircase k range of each output tile (Algorithm 6's band update:
-pith.science review of arXiv 2608.06291, Algorithm 6), T / S in the buffer of
-the node's depth.  Checked: every two steps that touch a tile, one of them
+pith.science review of arXiv 2608.06291, Algorithm 6), T / S in the node's T
+buffer (plan field 7).  Checked: every two steps that touch a tile, one of them
 writing it, are HB-ordered, writers of E and T before their readers, every W
 update of a tile before the leaf that reads it; the plan's band products cover
 exactly the tiles of the recursion nodes they come from.
@@ -148,10 +148,18 @@ def check_plan(m, n, order, mutate=None):
         for w in writers:
             for u in users:
                 assert u == w or hb(w, u) or hb(u, w), (m, n, key, steps[w], steps[u])
-        if key[0] in ("E", "T"):       # the single producer comes first
+        if key[0] == "E":              # the single producer comes first
             assert len(writers) == 1, key
             w = next(iter(writers))
             assert all(u == w or hb(w, u) for u in users), (m, n, key)
+        if key[0] == "T":              # T buffers are reused by later nodes: each
+            node = lambda k: (steps[k]["K"], steps[k]["L"])   # reader sees its own
+            for u in users - writers:                         # node's product, and
+                own = [w for w in writers if node(w) == node(u)]   # no other write
+                assert len(own) == 1, (m, n, key)             # lies in between
+                p = own[0]
+                assert hb(p, u), (m, n, key)
+                assert all(w == p or hb(u, w) or hb(w, p) for w in writers), (m, n, key)
         if key[0] == "W":              # every update before the leaf that reads the tile
             leaf = [k for k in users if steps[k]["kind"] == LEAF]
             assert len(leaf) == 1, key
@@ -229,3 +237,14 @@ def test_plan_check_catches_missing_sync(lib):
     for mutate in (fork, join):
         with pytest.raises(AssertionError):
             check_plan(4096, 4096, 1, mutate)
+
+
+def test_plan_check_catches_shared_t_buffer(lib):
+    # a deferred product keeps its node's T buffer while later nodes run: the
+    # model rejects a plan in which every node uses the same T buffer
+    def one_buffer(plan):
+        return [dict(op, depth=0) if op["kind"] == BAND else op for op in plan]
+    with pytest.raises(AssertionError):
+        check_plan(4096, 4096, 1, one_buffer)
+    with pytest.raises(AssertionError):
+        check_plan(4096, 4096, 2, one_buffer)

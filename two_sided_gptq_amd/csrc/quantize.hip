@@ -1159,22 +1159,23 @@ struct Node {
     int leaf;  // 1: leaf(K); 0: band(K, L, H)
     int flags;  // leaf only: LEAF_PUSH / LEAF_PULL (two-diagonal nodes run inside the leaves)
     int K, L, H;
-    int depth;  // band only: recursion depth (the top node is 0); selects its T buffer
+    int depth;  // band only: recursion depth (the top node is 0)
+    int slab;   // band only: its T buffer (set by build_plan)
 };
 
 void build_nodes(int K, int L, std::vector<Node> &out, int depth = 0) {
     if (L == 1) {
-        out.push_back({1, 0, K, 1, 0, depth});
+        out.push_back({1, 0, K, 1, 0, depth, 0});
         return;
     }
     if (L == 2) {  // leaf(K), band(K, 2, 1), leaf(K+1): the band runs inside the two leaves
-        out.push_back({1, LEAF_PUSH, K, 1, 0, depth});
-        out.push_back({1, LEAF_PULL, K + 1, 1, 0, depth});
+        out.push_back({1, LEAF_PUSH, K, 1, 0, depth, 0});
+        out.push_back({1, LEAF_PULL, K + 1, 1, 0, depth, 0});
         return;
     }
     const int H = L / 2;  // split of the range [K, K+L) at K + floor(L/2)
     build_nodes(K, H, out, depth + 1);
-    out.push_back({0, 0, K, L, H, depth});
+    out.push_back({0, 0, K, L, H, depth, 0});
     build_nodes(K + H, L - H, out, depth + 1);
 }
 
@@ -1223,9 +1224,13 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
 // and joined before the first critical step that updates or reads their
 // targets: the leaf of diagonal a, or a band node whose targets reach a.  So
 // the deferred products run while the leaves of K + H .. a - 1 hold a few CUs.
-// Nodes keep T in one buffer per recursion depth, so a deferred product shares
-// no T tile with the nodes that run meanwhile.  On one stream the same plan
-// gives the same results bit for bit.
+// A node that defers keeps T in the buffer of its recursion depth until its
+// deferred products are joined, which happens inside its right subtree, before
+// the next node of that depth starts; so a deferred product shares no T tile
+// with the nodes that run meanwhile.  Nodes below the deepest level that
+// defers run both products back to back on the critical stream and share one
+// more buffer: a solve needs (that level + 2) T buffers.  On one stream the
+// same plan gives the same results bit for bit.
 constexpr int OP_LEAF = 0, OP_BAND = 1, OP_RECORD = 2, OP_WAIT = 3;
 constexpr int SIDE_MIN_R = 16;
 // The deferred work should fit beside the leaves: the side kernel sustains
@@ -1249,12 +1254,18 @@ struct Op {
 struct Plan {
     std::vector<Op> ops;
     int events = 0;
+    int slabs = 1;  // T buffers
 };
 
 Plan build_plan(int M, int N, int shift) {
     Plan pl;
     std::vector<Node> nodes;
     build_nodes(0, M + N - 1, nodes);
+    int shared = 0;  // one past the deepest level with a deferring node
+    for (const Node &nd : nodes)
+        if (!nd.leaf && nd.L - nd.H >= SIDE_MIN_R) shared = std::max(shared, nd.depth + 1);
+    for (Node &nd : nodes) nd.slab = std::min(nd.depth, shared);
+    pl.slabs = shared + 1;
     std::vector<std::pair<int, int>> pending;  // (first target diagonal, completion event)
     auto join = [&](int upto) {  // the critical stream waits for deferred targets below upto
         for (size_t k = 0; k < pending.size();) {
@@ -1479,10 +1490,14 @@ struct Buffers {
     int nctr;
 };
 
-// T has one mp x np slab per recursion depth.
+// T has one mp x np slab per buffer of the plan (of the whole grid, or of the
+// parts of a split solve).
 size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     Carver cv(ws);
-    const int slabs = depth_of((int)(mp / TB + np / TB - 1));
+    const int M = (int)(mp / TB), N = (int)(np / TB);
+    int slabs = shape_info(M, N).plan.slabs;
+    if (N >= 2) slabs = std::max({slabs, shape_info(M, N / 2).plan.slabs, shape_info(M, N - N / 2).plan.slabs});
+    if (M >= 2) slabs = std::max({slabs, shape_info(M / 2, N).plan.slabs, shape_info(M - M / 2, N).plan.slabs});
     float *Wp = cv.take<float>(mp * np);
     float *Eb = cv.take<float>(mp * np);
     float *Tb = cv.take<float>(mp * np * slabs);
@@ -1494,7 +1509,6 @@ size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     float *Cd = cv.take<float>(mp * np);
     float *Cr = cv.take<float>(mp * np);
     // counters for the plan of the whole grid and of the parts of a split solve
-    const int M = (int)(mp / TB), N = (int)(np / TB);
     int nctr = std::max(1, shape_info(M, N).side_ops);
     if (N >= 2) nctr = std::max({nctr, shape_info(M, N / 2).side_ops, shape_info(M, N - N / 2).side_ops});
     if (M >= 2) nctr = std::max({nctr, shape_info(M / 2, N).side_ops, shape_info(M - M / 2, N).side_ops});
@@ -1575,7 +1589,7 @@ extern "C" int32_t bakron_schedule_plan(int64_t m, int64_t n, int32_t flags, int
             o[3] = op.nd.K;
             o[4] = op.nd.flags;
         } else if (op.kind == OP_BAND) {
-            o[3] = op.nd.K; o[5] = op.nd.L; o[6] = op.nd.H; o[7] = op.nd.depth;
+            o[3] = op.nd.K; o[5] = op.nd.L; o[6] = op.nd.H; o[7] = op.nd.slab;
             o[8] = op.prod; o[9] = op.lo; o[10] = op.hi;
             int mode, olo, cols, rlo, rows;
             if (band_geometry(op, order, M, N, mode, olo, cols, rlo, rows)) {
@@ -1850,6 +1864,7 @@ struct GraphKey {
 
 struct GraphEntry {
     hipGraphExec_t exec;
+    hipEvent_t done;  // recorded on the launch stream after every launch
     uint64_t last_use;
 };
 
@@ -1882,52 +1897,63 @@ int32_t make_stream(hipStream_t *s) {
     return BAKRON_OK;
 }
 
-// Finds or builds the graph for `sv`; returns it through `exec`.
-int32_t graph_for(const Solve &sv, int dev, const void *ws, hipGraphExec_t *exec) {
+// Finds or builds the graph for `sv` and launches it on `stream`.  Lookup,
+// capture, eviction and launch all happen under g_graph_mu, so no thread can
+// destroy an executable graph between another thread's lookup and launch; an
+// evicted graph is destroyed only after its last launch has completed.
+int32_t launch_graph(const Solve &sv, int dev, const void *ws, hipStream_t stream) {
     GraphKey key{dev, sv.order, sv.qkind, sv.qbits, sv.mse, sv.split, sv.m, sv.n,
                  {sv.W, sv.LA, sv.LB, sv.codes, sv.scales, sv.zeros, sv.V, sv.E, sv.sum_e2,
                   sv.dev_status, ws, nullptr}};
     std::lock_guard<std::mutex> lock(g_graph_mu);
     auto it = g_graphs.find(key);
-    if (it != g_graphs.end()) {
-        it->second.last_use = ++g_graph_clock;
-        *exec = it->second.exec;
-        return BAKRON_OK;
+    if (it == g_graphs.end()) {
+        DevStreams &ds = g_dev[dev];
+        int32_t st = make_stream(&ds.cap);
+        if (st == BAKRON_OK) st = make_stream(&ds.cap_side);
+        if (st == BAKRON_OK) st = grow_events(ds.cap_ev, solve_events(sv));
+        if (st != BAKRON_OK) return st;
+        hipStream_t cs = ds.cap;
+        BK_HIP_CHECK(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
+        st = enqueue_solve(sv, cs, ds.cap_side, &ds.cap_ev, nullptr, nullptr);
+        hipGraph_t graph = nullptr;
+        hipError_t ce = hipStreamEndCapture(cs, &graph);
+        if (st != BAKRON_OK) {
+            if (graph) (void)hipGraphDestroy(graph);
+            return st;
+        }
+        if (ce != hipSuccess) {
+            set_error("hipStreamEndCapture: %s", hipGetErrorString(ce));
+            return BAKRON_ERR_HIP;
+        }
+        hipGraphExec_t ge;
+        hipError_t ie = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (ie != hipSuccess) {
+            set_error("hipGraphInstantiate: %s", hipGetErrorString(ie));
+            return BAKRON_ERR_HIP;
+        }
+        hipEvent_t done;
+        ie = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+        if (ie != hipSuccess) {
+            (void)hipGraphExecDestroy(ge);
+            set_error("hipEventCreateWithFlags: %s", hipGetErrorString(ie));
+            return BAKRON_ERR_HIP;
+        }
+        if (g_graphs.size() >= kGraphCache) {
+            auto victim = g_graphs.begin();
+            for (auto jt = g_graphs.begin(); jt != g_graphs.end(); ++jt)
+                if (jt->second.last_use < victim->second.last_use) victim = jt;
+            (void)hipEventSynchronize(victim->second.done);
+            (void)hipGraphExecDestroy(victim->second.exec);
+            (void)hipEventDestroy(victim->second.done);
+            g_graphs.erase(victim);
+        }
+        it = g_graphs.emplace(key, GraphEntry{ge, done, 0}).first;
     }
-    DevStreams &ds = g_dev[dev];
-    int32_t st = make_stream(&ds.cap);
-    if (st == BAKRON_OK) st = make_stream(&ds.cap_side);
-    if (st == BAKRON_OK) st = grow_events(ds.cap_ev, solve_events(sv));
-    if (st != BAKRON_OK) return st;
-    hipStream_t cs = ds.cap;
-    BK_HIP_CHECK(hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal));
-    st = enqueue_solve(sv, cs, ds.cap_side, &ds.cap_ev, nullptr, nullptr);
-    hipGraph_t graph = nullptr;
-    hipError_t ce = hipStreamEndCapture(cs, &graph);
-    if (st != BAKRON_OK) {
-        if (graph) (void)hipGraphDestroy(graph);
-        return st;
-    }
-    if (ce != hipSuccess) {
-        set_error("hipStreamEndCapture: %s", hipGetErrorString(ce));
-        return BAKRON_ERR_HIP;
-    }
-    hipGraphExec_t ge;
-    hipError_t ie = hipGraphInstantiate(&ge, graph, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(graph);
-    if (ie != hipSuccess) {
-        set_error("hipGraphInstantiate: %s", hipGetErrorString(ie));
-        return BAKRON_ERR_HIP;
-    }
-    if (g_graphs.size() >= kGraphCache) {
-        auto victim = g_graphs.begin();
-        for (auto jt = g_graphs.begin(); jt != g_graphs.end(); ++jt)
-            if (jt->second.last_use < victim->second.last_use) victim = jt;
-        (void)hipGraphExecDestroy(victim->second.exec);
-        g_graphs.erase(victim);
-    }
-    g_graphs[key] = GraphEntry{ge, ++g_graph_clock};
-    *exec = ge;
+    it->second.last_use = ++g_graph_clock;
+    BK_HIP_CHECK(hipGraphLaunch(it->second.exec, stream));
+    BK_HIP_CHECK(hipEventRecord(it->second.done, stream));
     return BAKRON_OK;
 }
 
@@ -1940,7 +1966,7 @@ int32_t launch_band(const Solve &sv, const Op &op, int *ctr, hipStream_t stream,
     int mode, olo, cols, rlo, rows;
     *launched = 0;
     if (!band_geometry(op, sv.order, M, N, mode, olo, cols, rlo, rows)) return BAKRON_OK;
-    float *T = b.Tbuf + (int64_t)nd.depth * mp * np;
+    float *T = b.Tbuf + (int64_t)nd.slab * mp * np;
     BandArgs g{};
     switch (mode) {
     case 0: g = BandArgs{b.LAp, b.Ebuf, T, np, np, mp, 0, nd.K, nd.L, nd.H, M, N, rlo, 0, rows, olo, cols}; break;
@@ -2124,11 +2150,7 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
         if (st != BAKRON_OK) return st;
         return enqueue_solve(sv, stream, ds->side, &ds->ev, nullptr, nullptr);
     }
-    hipGraphExec_t exec;
-    st = graph_for(sv, dev, ws, &exec);
-    if (st != BAKRON_OK) return st;
-    BK_HIP_CHECK(hipGraphLaunch(exec, stream));
-    return BAKRON_OK;
+    return launch_graph(sv, dev, ws, stream);
 }
 
 // --------------------------------------------------------------------------
