@@ -165,6 +165,33 @@ int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
                         int32_t flags, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * bakron_quantize_noalloc -- bakron_quantize for callers that cannot allocate
+ * device memory: code under HIP stream capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as bakron_quantize, without
+ * the workspace; the flags BAKRON_ORDER_*, BAKRON_FLAG_MSE_SCALE and
+ * BAKRON_FLAG_SPLIT_* (BAKRON_FLAG_NO_GRAPH is accepted and changes nothing).
+ *   - The solve's scratch is a fixed array of BAKRON_NOALLOC_SCRATCH_BYTES in
+ *     device memory, inside the library: each GPU it runs on holds one copy
+ *     until the process ends.  A shape whose workspace
+ *     (bakron_quantize_workspace_size) exceeds it is rejected with
+ *     BAKRON_ERR_WORKSPACE before anything is enqueued (2048 x 2048 fits,
+ *     4096 x 4096 does not).
+ *   - The plan runs in order on `stream` alone: no side stream, no event, no
+ *     graph.  The results equal bakron_quantize's bit for bit.
+ *   - It calls no hipMalloc, hipFree or other allocating routine.
+ *   - Every call on one GPU uses that GPU's array, which keeps the last call's
+ *     contents (what must start at zero is cleared by each call).  Calls that
+ *     overlap on one GPU (other streams, other host threads) race on it and
+ *     give wrong results: serialise them.
+ * Returns as bakron_quantize; BAKRON_FLAG_PHASE_TIMING is rejected.
+ */
+#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int32_t bakron_quantize_noalloc(const float *W, int64_t m, int64_t n, const float *LA,
+                                const float *LB, int32_t qkind, int32_t qbits, int8_t *codes,
+                                float *scales, float *zeros, float *V, float *E, double *sum_e2,
+                                int32_t *dev_status, int32_t flags, void *stream);
+
+/*
  * bakron_quantize_antidiag -- BaKron-antidiagonal, the pages' comparison
  * variant (review page "If this is right": BaKron runs about 27x faster than
  * it at 4096 x 4096; "Core claim", Theorem 3.2: both give the same output).

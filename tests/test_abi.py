@@ -188,3 +188,24 @@ def test_schedule_shape(lib):
     steps = [bakron.schedule_info(k, k)["leaf_steps"] for k in (1024, 2048, 4096, 8192)]
     for a, b in zip(steps, steps[1:]):
         assert 1.9 < b / a < 2.1
+
+
+def test_noalloc_argument_errors_without_device(lib):
+    """The allocation-free entry point validates before touching a device: too
+    large a shape for its fixed scratch is BAKRON_ERR_WORKSPACE, timing and
+    unknown flags are invalid arguments."""
+    fake = ctypes.c_void_p(4096)
+    args = lambda m, n, flags: (fake, m, n, fake, fake, 0, 4, fake, fake, None, None, None, None,
+                                None, flags, None)
+    assert bakron.NOALLOC_SCRATCH_BYTES == 256 << 20
+    assert lib.bakron_quantize_workspace_size(2048, 2048, 0, 4) <= bakron.NOALLOC_SCRATCH_BYTES
+    assert lib.bakron_quantize_workspace_size(4096, 4096, 0, 4) > bakron.NOALLOC_SCRATCH_BYTES
+    rc = lib.bakron_quantize_noalloc(*args(4096, 4096, 0))
+    assert rc == 2 and b"bakron_quantize_noalloc has" in lib.bakron_last_error()
+    rc = lib.bakron_quantize_noalloc(*args(64, 64, 0x4))
+    assert rc == 1 and b"PHASE_TIMING" in lib.bakron_last_error()
+    rc = lib.bakron_quantize_noalloc(*args(64, 64, 0x80))
+    assert rc == 1
+    rc = lib.bakron_quantize_noalloc(None, 64, 64, fake, fake, 0, 4, fake, fake, None, None, None,
+                                     None, None, 0, None)
+    assert rc == 1 and b"non-NULL" in lib.bakron_last_error()

@@ -27,7 +27,7 @@ DEV_NONFINITE, DEV_NOT_PD = 1, 2
 EXPORTS = (
     "bakron_hessian_workspace_size", "bakron_hessian",
     "bakron_factor_workspace_size", "bakron_factor",
-    "bakron_quantize_workspace_size", "bakron_quantize",
+    "bakron_quantize_workspace_size", "bakron_quantize", "bakron_quantize_noalloc",
     "bakron_quantize_antidiag_workspace_size", "bakron_quantize_antidiag",
     "bakron_schedule_info", "bakron_schedule_plan", "bakron_last_phase_ms",
     "bakron_status_string", "bakron_last_error",
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bakron_quantize_workspace_size.restype = SZ
     lib.bakron_quantize.argtypes = [P, I64, I64, P, P, I32, I32, P, P, P, P, P, P, P, I32, P, SZ, P]
     lib.bakron_quantize.restype = I32
+    lib.bakron_quantize_noalloc.argtypes = [P, I64, I64, P, P, I32, I32, P, P, P, P, P, P, P, I32, P]
+    lib.bakron_quantize_noalloc.restype = I32
     lib.bakron_quantize_antidiag_workspace_size.argtypes = [I64, I64, I32, I32]
     lib.bakron_quantize_antidiag_workspace_size.restype = SZ
     lib.bakron_quantize_antidiag.argtypes = [P, I64, I64, P, P, I32, I32, P, P, P, P, P, P, P, SZ, P]
@@ -169,6 +171,41 @@ def quantize(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_
                              _ptr(out["E"]), _ptr(out["sum_e2"]), _ptr(dev_status), flags,
                              _ptr(workspace), workspace.numel(), _stream(stream))
     _check(rc, "bakron_quantize")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20  # BAKRON_NOALLOC_SCRATCH_BYTES
+
+
+def quantize_noalloc(W, LA, LB, kind=Q_SYM, bits=4, order=ORDER_AUTO, want_V=True, want_E=False,
+                     want_sum=False, dev_status=None, out=None, stream=None, mse=False, split=None):
+    """Run bakron_quantize_noalloc (no workspace: the library's fixed scratch
+    array; the plan in order on one stream).  Outputs as for quantize(); pass
+    ``out`` to reuse preallocated output tensors."""
+    lib = load()
+    W = _f32_dev(W, "W")
+    LA = _f32_dev(LA, "LA")
+    LB = _f32_dev(LB, "LB")
+    m, n = W.shape
+    dev = W.device
+    if out is None:
+        out = dict(
+            codes=torch.empty((m, n), dtype=torch.int8, device=dev),
+            scales=torch.empty(m, dtype=torch.float32, device=dev),
+            zeros=torch.empty(m, dtype=torch.float32, device=dev) if kind == Q_ASYM else None,
+            V=torch.empty((m, n), dtype=torch.float32, device=dev) if want_V else None,
+            E=torch.empty((m, n), dtype=torch.float32, device=dev) if want_E else None,
+            sum_e2=torch.empty(1, dtype=torch.float64, device=dev) if want_sum else None,
+        )
+    if split not in (None, "cols", "rows"):
+        raise ValueError(f"split must be None, 'cols' or 'rows', not {split!r}")
+    flags = (int(order) | (FLAG_MSE_SCALE if mse else 0) | (FLAG_SPLIT_COLS if split == "cols" else 0) |
+             (FLAG_SPLIT_ROWS if split == "rows" else 0))
+    rc = lib.bakron_quantize_noalloc(_ptr(W), m, n, _ptr(LA), _ptr(LB), kind, bits, _ptr(out["codes"]),
+                                     _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["V"]),
+                                     _ptr(out["E"]), _ptr(out["sum_e2"]), _ptr(dev_status), flags,
+                                     _stream(stream))
+    _check(rc, "bakron_quantize_noalloc")
     return out
 
 

@@ -2053,12 +2053,15 @@ int32_t replay_band(const Solve &sv, int dev, hipStream_t stream, int side, doub
 }  // namespace
 }  // namespace bakron
 
-extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
-                                   const float *LB, int32_t qkind, int32_t qbits, int8_t *codes,
-                                   float *scales, float *zeros, float *V, float *E,
-                                   double *sum_e2, int32_t *dev_status, int32_t flags, void *ws,
-                                   size_t ws_bytes, void *stream_) {
-    clear_error();
+namespace bakron {
+namespace {
+
+// Argument checks shared by bakron_quantize and bakron_quantize_noalloc, then
+// the solve's description (without its workspace buffers).
+int32_t make_solve(const float *W, int64_t m, int64_t n, const float *LA, const float *LB,
+                   int32_t qkind, int32_t qbits, int8_t *codes, float *scales, float *zeros,
+                   float *V, float *E, double *sum_e2, int32_t *dev_status, int32_t flags,
+                   Solve *out) {
     BK_REQUIRE(W && LA && LB && codes && scales, "W, LA, LB, codes and scales must be non-NULL");
     BK_REQUIRE(m >= 1 && n >= 1 && m <= MAX_DIM && n <= MAX_DIM, "bad shape %lld x %lld",
                (long long)m, (long long)n);
@@ -2072,16 +2075,6 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     BK_REQUIRE(!((flags & (BAKRON_FLAG_SPLIT_COLS | BAKRON_FLAG_SPLIT_ROWS)) &&
                  (flags & BAKRON_FLAG_PHASE_TIMING)),
                "BAKRON_FLAG_PHASE_TIMING times the unsplit schedule only (no BAKRON_FLAG_SPLIT_*)");
-    const size_t need = bakron_quantize_workspace_size(m, n, qkind, qbits);
-    if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
-        set_error("workspace needs %zu bytes at 256-byte alignment (got %zu at %p)", need,
-                  ws_bytes, ws);
-        return BAKRON_ERR_WORKSPACE;
-    }
-    int32_t st = check_device();
-    if (st != BAKRON_OK) return st;
-
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
     Solve sv{};
     sv.W = W; sv.LA = LA; sv.LB = LB; sv.m = m; sv.n = n;
     sv.mp = round_up(m, TB);
@@ -2104,6 +2097,32 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
     sv.split = (flags & BAKRON_FLAG_SPLIT_COLS) && sv.N >= 2   ? SPLIT_COLS
                : (flags & BAKRON_FLAG_SPLIT_ROWS) && sv.M >= 2 ? SPLIT_ROWS
                                                                : SPLIT_NONE;
+    *out = sv;
+    return BAKRON_OK;
+}
+
+}  // namespace
+}  // namespace bakron
+
+extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const float *LA,
+                                   const float *LB, int32_t qkind, int32_t qbits, int8_t *codes,
+                                   float *scales, float *zeros, float *V, float *E,
+                                   double *sum_e2, int32_t *dev_status, int32_t flags, void *ws,
+                                   size_t ws_bytes, void *stream_) {
+    clear_error();
+    Solve sv{};
+    int32_t st = make_solve(W, m, n, LA, LB, qkind, qbits, codes, scales, zeros, V, E, sum_e2,
+                            dev_status, flags, &sv);
+    if (st != BAKRON_OK) return st;
+    const size_t need = bakron_quantize_workspace_size(m, n, qkind, qbits);
+    if (ws == nullptr || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255) != 0) {
+        set_error("workspace needs %zu bytes at 256-byte alignment (got %zu at %p)", need,
+                  ws_bytes, ws);
+        return BAKRON_ERR_WORKSPACE;
+    }
+    st = check_device();
+    if (st != BAKRON_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
     carve(ws, sv.mp, sv.np, &sv.b);
 
     if (flags & BAKRON_FLAG_PHASE_TIMING) {
@@ -2151,6 +2170,76 @@ extern "C" int32_t bakron_quantize(const float *W, int64_t m, int64_t n, const f
         return enqueue_solve(sv, stream, ds->side, &ds->ev, nullptr, nullptr);
     }
     return launch_graph(sv, dev, ws, stream);
+}
+
+// --------------------------------------------------------------------------
+// bakron_quantize_noalloc: the solve for callers that cannot allocate device
+// memory.  Its workspace is `scratch`, a fixed array of device memory: each
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code the name `scratch` denotes a host-side stand-in, not a device address;
+// the device address of the current GPU's copy comes from
+// hipGetSymbolAddress, taken once per device (that device current) on the
+// entry point's first call there, and only that address reaches the kernels.
+static __device__ __align__(256) unsigned char scratch[BAKRON_NOALLOC_SCRATCH_BYTES];
+
+namespace bakron {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+int32_t scratch_address(void **ptr) {
+    int dev = 0;
+    BK_HIP_CHECK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("device index %d out of range", dev);
+        return BAKRON_ERR_UNSUPPORTED_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        BK_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255) != 0) {
+            set_error("hipGetSymbolAddress(scratch) gave %p", p);
+            return BAKRON_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return BAKRON_OK;
+}
+
+}  // namespace
+}  // namespace bakron
+
+extern "C" int32_t bakron_quantize_noalloc(const float *W, int64_t m, int64_t n, const float *LA,
+                                           const float *LB, int32_t qkind, int32_t qbits,
+                                           int8_t *codes, float *scales, float *zeros, float *V,
+                                           float *E, double *sum_e2, int32_t *dev_status,
+                                           int32_t flags, void *stream_) {
+    clear_error();
+    BK_REQUIRE(!(flags & BAKRON_FLAG_PHASE_TIMING),
+               "BAKRON_FLAG_PHASE_TIMING creates events; bakron_quantize_noalloc does not take it");
+    Solve sv{};
+    int32_t st = make_solve(W, m, n, LA, LB, qkind, qbits, codes, scales, zeros, V, E, sum_e2,
+                            dev_status, flags, &sv);
+    if (st != BAKRON_OK) return st;
+    const size_t need = bakron_quantize_workspace_size(m, n, qkind, qbits);
+    if (need > BAKRON_NOALLOC_SCRATCH_BYTES) {
+        set_error("a %lld x %lld solve needs %zu bytes of workspace; bakron_quantize_noalloc has "
+                  "%zu (use bakron_quantize with a workspace)",
+                  (long long)m, (long long)n, need, (size_t)BAKRON_NOALLOC_SCRATCH_BYTES);
+        return BAKRON_ERR_WORKSPACE;
+    }
+    st = check_device();
+    if (st != BAKRON_OK) return st;
+    void *ptr = nullptr;
+    st = scratch_address(&ptr);
+    if (st != BAKRON_OK) return st;
+    carve(ptr, sv.mp, sv.np, &sv.b);
+    // the plan in order on the caller's stream: no side stream, event or graph
+    return enqueue_solve(sv, static_cast<hipStream_t>(stream_), nullptr, nullptr, nullptr, nullptr);
 }
 
 // --------------------------------------------------------------------------
