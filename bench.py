@@ -18,6 +18,9 @@ Prints one JSON line.  Besides the contract fields it carries
                 chain of dependent steps, not by a throughput roofline
   leaf          the leaf phase: HBM bytes per launch, launches, in-kernel steps,
                 and its in-tile flops against the fp32 vector peak
+  prep          bakron_hessian and bakron_factor for both Kronecker factors,
+                each timed on its own (they sit on either side of the solve and
+                are not part of a step)
   cpu_baseline  the fp64 oracle (BaKron-naive) on a bounded leading block of
                 the same problem, on this host's cores
 """
@@ -102,16 +105,41 @@ def main():
     dev = torch.device("cuda:0")
     bakron.load()
 
-    # ---- synthetic inputs and factors (untimed)
+    # ---- synthetic inputs and factors (outside the timed steps; each hessian
+    # and factor call is timed on its own after one warm-up call)
     W_h = synth.weights(w)
     X = torch.from_numpy(synth.input_samples(w)).to(dev)
     Y_h = synth.output_samples(w)
-    LA = bakron.factor(bakron.hessian(X, synth.DAMP))
+    prep = {}
+
+    def timed(label, fn, flops):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        prep[label] = {"ms": ms, "tflops": flops / (ms / 1e3) / 1e12 if flops else None}
+        return r
+
+    # Gram product: 2 N d^2 flops for the full product (N d (d + 1) for one
+    # triangle); factor: Cholesky plus triangular inverse, d^3 flops
+    HA = timed("hessian_A", lambda: bakron.hessian(X, synth.DAMP), 2.0 * X.shape[0] * w.n ** 2)
+    prep["hessian_A"].update(N=int(X.shape[0]), d=w.n)
+    LA = timed("factor_A", lambda: bakron.factor(HA), float(w.n) ** 3)
+    prep["factor_A"].update(d=w.n)
     if Y_h is None:
         LB = torch.eye(w.m, dtype=torch.float32, device=dev)
     else:
-        LB = bakron.factor(bakron.hessian(torch.from_numpy(Y_h).to(dev), synth.DAMP))
-    del X
+        Y = torch.from_numpy(Y_h).to(dev)
+        HB = timed("hessian_B", lambda: bakron.hessian(Y, synth.DAMP), 2.0 * Y.shape[0] * w.m ** 2)
+        prep["hessian_B"].update(N=int(Y.shape[0]), d=w.m)
+        LB = timed("factor_B", lambda: bakron.factor(HB), float(w.m) ** 3)
+        prep["factor_B"].update(d=w.m)
+        del Y, HB
+    del X, HA
     W = torch.from_numpy(W_h).to(dev)
     m, n = w.m, w.n
     status = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -173,8 +201,9 @@ def main():
                    if ph["side_launches"] else None)
     leaf_avg_s = ph["leaf_ms"] / 1e3 / sched["leaf_launches"]
     # leaf algorithmic HBM bytes per entry: W tile in (4), E out (4), codes (1),
-    # V (4), plus the two diagonal 64 x 64 factor blocks per tile (2 x 4 / 64 per entry)
-    leaf_bytes = m * n * (4 + 4 + 1 + 4 + 8.0 / 64)
+    # V (4), and the lower triangles of the two diagonal 64 x 64 factor blocks of
+    # each tile (2 x 64 x 65 / 2 floats per 4096 entries, about 4)
+    leaf_bytes = m * n * (4 + 4 + 1 + 4 + 2 * 4.0 * (64 * 65 / 2) / (64 * 64))
     leaf_gbs = leaf_bytes / sched["leaf_launches"] / leaf_avg_s / 1e9
     dominant = "band_gemm" if ph["band_ms"] >= ph["leaf_ms"] else "leaf"
     # HBM bytes per band-GEMM dispatch from the committed rocprofv3 counter
@@ -226,6 +255,9 @@ def main():
                  "avg_launch_ms": leaf_avg_s * 1e3, "alg_bytes": leaf_bytes,
                  "achieved_GBs": leaf_gbs, "hbm_frac": leaf_gbs / HBM_PEAK_GBS},
         "schedule": sched,
+        "prep": prep,
+        "hessian_ms": sum(v["ms"] for k, v in prep.items() if k.startswith("hessian")),
+        "factor_ms": sum(v["ms"] for k, v in prep.items() if k.startswith("factor")),
     }
     if args.antidiag:
         # the pages' comparison (review page, "If this is right": BaKron about 27x

@@ -46,6 +46,12 @@ def test_report_fields():
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 157.3
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
     assert 0 < rf["frac"] < 1
+    # the leaf's algorithmic bytes: W in, E, codes, V out, and the lower
+    # triangles of the two diagonal factor blocks of each 64 x 64 tile
+    assert r["leaf"]["alg_bytes"] == r["config"]["m"] * r["config"]["n"] * (13 + 8 * 2080 / 4096)
+    # hessian and factor timed apart from the solve, for both sides
+    assert r["hessian_ms"] > 0 and r["factor_ms"] > 0
+    assert set(r["prep"]) == {"hessian_A", "factor_A", "hessian_B", "factor_B"}
     cb = r["cpu_baseline"]
     for k in ("value", "unit", "cores", "kind", "sample"):
         assert k in cb, k

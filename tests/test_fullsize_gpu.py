@@ -19,11 +19,14 @@ verify the whole output up to floating-point tolerance:
   rounding     every code is the base quantizer of V + LB_ii LA_jj E_ij;
   loss         tr((V-W)^T B (V-W) A), with A and B the oracle's fp64 Gram
                matrices of the same samples, equals sum e^2 within a tolerance
-               derived from how far the fp32 factors are from exact
-               (||L^T H L - I||_2) and from the completion residual, and
-               within 1e-3 relative;
+               derived from how far the pipeline's fp32 factors are from exact
+               for those matrices (||L^T H L - I||_2) and from the completion
+               residual, and within 1e-3 relative;
   factors      the library's factors at these sizes satisfy L^T H L = I to
-               1e-3 in the 2-norm, with H the oracle's fp64 Gram matrix;
+               1e-3 in the 2-norm for the fp32 matrix H they were computed
+               from (the library's fp32 Gram product, whose own rounding moves
+               the ill-conditioned output-side factors further from the fp64
+               Gram matrices: that part enters the loss tolerance);
   replay       a second call into the same buffers (a cached-graph replay)
                reproduces the first bitwise.
 """
@@ -81,8 +84,9 @@ def solved(bk):
         W = synth.weights(w)
         Xh = synth.input_samples(w)
         Yh = synth.output_samples(w)
-        LA = bk.factor(bk.hessian(torch.from_numpy(Xh).cuda(), synth.DAMP))
-        LB = bk.factor(bk.hessian(torch.from_numpy(Yh).cuda(), synth.DAMP))
+        HA = bk.hessian(torch.from_numpy(Xh).cuda(), synth.DAMP)
+        HB = bk.hessian(torch.from_numpy(Yh).cuda(), synth.DAMP)
+        LA, LB = bk.factor(HA), bk.factor(HB)
         status = torch.zeros(1, dtype=torch.int32, device="cuda")
         Wd = torch.from_numpy(W).cuda()
         ws = torch.empty(bk.quantize_workspace_size(w.m, w.n, w.qkind, w.qbits), dtype=torch.uint8,
@@ -99,8 +103,9 @@ def solved(bk):
         replay_equal = all(torch.equal(v, out[k]) for k, v in first.items())
         h = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
         h["zeros"] = h["zeros"] if "zeros" in h else np.zeros(w.m, np.float32)
-        h.update(W=W, LA=LA.cpu().numpy(), LB=LB.cpu().numpy(), replay_equal=replay_equal, w=w)
-        del Wd, ws, out, first, LA, LB
+        h.update(W=W, LA=LA.cpu().numpy(), LB=LB.cpu().numpy(), HA=HA.cpu().numpy(),
+                 HB=HB.cpu().numpy(), replay_equal=replay_equal, w=w)
+        del Wd, ws, out, first, LA, LB, HA, HB
         torch.cuda.empty_cache()
         print(f"[fullsize] {name}: GPU part {time.time() - t0:.1f} s", flush=True)
         t0 = time.time()
@@ -177,13 +182,18 @@ def test_fullsize_loss_and_factors(solved, name):
     h = solved(name)
     A, B, LAh, LBh = h["A"], h["B"], h["LA"], h["LB"]
     t0 = time.time()
+    facA = _factor_defect(LAh, h["HA"].astype(np.float64))
+    facB = _factor_defect(LBh, h["HB"].astype(np.float64))
     rhoA = _factor_defect(LAh, A)
     rhoB = _factor_defect(LBh, B)
     normA = _spectral_norm(lambda x: A @ x, A.shape[0])
     normB = _spectral_norm(lambda x: B @ x, B.shape[0])
-    print(f"[fullsize] {name}: ||LA^T A LA - I|| {rhoA:.3e}, ||LB^T B LB - I|| {rhoB:.3e} "
+    print(f"[fullsize] {name}: factor of its own input: ||LA^T HA LA - I|| {facA:.3e}, "
+          f"||LB^T HB LB - I|| {facB:.3e}; against the fp64 Gram matrices: {rhoA:.3e}, {rhoB:.3e} "
           f"({time.time() - t0:.1f} s)", flush=True)
-    assert rhoA < 1e-3 and rhoB < 1e-3
+    # rounding the exact factor to fp32 alone leaves about 2^-24 sqrt(cond H)
+    # (about 3e-5 for the 11008 x 11008 output side, cond ~ 3e5)
+    assert facA < 1e-3 and facB < 1e-3
 
     t0 = time.time()
     W, V, E = h["W"], h["V"], h["E"]
