@@ -83,3 +83,42 @@ def test_full_pipeline_c2(bk):
     bad, ties = oracle.rounding_consistency(codes, V, E, np.diag(LAh), np.diag(LBh), s,
                                             np.zeros_like(s), w.qkind, w.qbits)
     assert bad == 0
+
+
+def test_hessian_and_factor_at_config_size(bk):
+    """The 4096 x 4096 workload's input side (8192 samples, 32 outlier channels
+    x20): the Gram matrix on sampled entries (every outlier pair, the diagonal,
+    random entries) against the oracle's fp64 entries, exact symmetry, then the
+    factor of that fp32 matrix against the oracle's fp64 chol(inv(H)) and the
+    residual L^T H L - I."""
+    w = synth.WORKLOADS["c3"]
+    X = synth.input_samples(w)
+    Xd = torch.from_numpy(X).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    H = bk.hessian(Xd, synth.DAMP)
+    L = bk.factor(H, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    Hg = H.cpu().numpy()
+    assert np.array_equal(Hg, Hg.T)
+    d = Hg.shape[0]
+    g = np.random.default_rng(41)
+    big = np.nonzero(np.abs(X[:64]).max(axis=0) > 10)[0]        # the outlier channels
+    rows = np.concatenate([np.repeat(big, len(big)), np.arange(d), g.integers(0, d, 3000)])
+    cols = np.concatenate([np.tile(big, len(big)), np.arange(d), g.integers(0, d, 3000)])
+    ho = oracle.hessian_entries(X, rows, cols, synth.DAMP)
+    diag = np.diag(Hg).astype(np.float64)
+    err = np.max(np.abs(Hg[rows, cols] - ho) / np.sqrt(diag[rows] * diag[cols]))
+    print(f"[config] hessian 8192 x 4096: max relative error {err:.3e} ({len(big)} outlier channels)")
+    assert len(big) == w.outliers and err < 2e-5
+
+    Lg = L.cpu().numpy().astype(np.float64)
+    H64 = Hg.astype(np.float64)
+    Lo = oracle.factor(H64)
+    assert np.array_equal(np.triu(Lg, 1), np.zeros_like(Lg)) and np.all(np.diag(Lg) > 0)
+    ferr = np.max(np.abs(Lg - Lo)) / np.max(np.abs(Lo))
+    R = Lg.T @ H64 @ Lg - np.eye(d)
+    print(f"[config] factor d = 4096: max |L - L_oracle| / max |L_oracle| {ferr:.3e}, "
+          f"max |L^T H L - I| {np.max(np.abs(R)):.3e}")
+    assert ferr < 1e-6
+    assert np.max(np.abs(R)) < 1e-4
