@@ -456,6 +456,14 @@ __device__ __forceinline__ void unit_dots(const float *X, const float *const (&Y
     }
 }
 
+// Helper units come in groups of four: (row or column idx, idx + 1) x (row
+// direction, column direction).  The two units in one 8-lane half of a group
+// share the direction, so their operand rows (idx and idx + 1, 80 floats
+// apart) fall in different LDS banks; units of the two directions at one idx
+// read arrays that start in the same bank.
+__device__ __forceinline__ int unit_idx(int u) { return 2 * (u >> 2) + (u & 1); }
+__device__ __forceinline__ int unit_dir(int u) { return (u >> 1) & 1; }
+
 // One helper unit: 4 lanes (q = 0..3) compute the LJ bulk dots of one row
 // (dir 0, row direction, X = E[idx][.], Y = LA rows of the entries' columns) or
 // one column (dir 1, column direction, X = Z[.][idx], Y = LB rows of the
@@ -463,7 +471,7 @@ __device__ __forceinline__ void unit_dots(const float *X, const float *const (&Y
 // nch (at least ceil(len / 16)) is uniform over the wave.
 __device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float *buf, int q,
                                             int nch) {
-    const int idx = lo + (u >> 1), dir = u & 1;
+    const int idx = lo + unit_idx(u), dir = unit_dir(u);
     const int len = s0 - idx;
     const float *X = (dir ? lf_Z : lf_E) + idx * LP + 4 * q;
     const float *Yb = (dir ? lf_B : lf_A) + 4 * q;
@@ -510,14 +518,15 @@ __device__ __forceinline__ void leaf_helpers(const int w, const int lane) {
             // bulk of block t+1: diagonals D0 .. D0+LJ-1, terms of steps < s0
             const int D0 = LJ * (t + 1), s0 = LJ * t;
             const int lo = max(0, D0 - (TB - 1)), hi = min(TB - 1, D0 + LJ - 1);
-            const int nunit = 2 * (hi - lo + 1);
+            const int nrow = hi - lo + 1;
+            const int nunit = 4 * ((nrow + 1) >> 1);
             float *buf = lf_bulk + ((t + 1) & 1) * 2 * TB * LJ;
             // lane 0 of the wave holds its longest unit, whose chunk count every
             // group of the wave uses
             const int g0 = __builtin_amdgcn_readfirstlane(g);
-            const int len0 = s0 - (lo + (g0 >> 1));
+            const int len0 = s0 - (lo + unit_idx(g0));
             const int nch = len0 > 0 ? (len0 + 15) >> 4 : 0;
-            if (g < nunit) helper_unit(g, lo, D0, s0, buf, q, nch);
+            if (g < nunit && unit_idx(g) < nrow) helper_unit(g, lo, D0, s0, buf, q, nch);
         }
         __syncthreads();
     }
@@ -891,12 +900,17 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
 // (or SIDE_WG_QUARTER) workgroups of 1024 threads, and each workgroup's LDS
 // (four tiles' operand blocks, 139 KB) keeps it alone on its CU, so a side
 // launch leaves at least 64 CUs to the leaves (one workgroup of 160 KB LDS
-// per tile; a tile diagonal of up to 64 tiles finds them empty).  The four 4-wave slots of a workgroup work independently,
-// like four workgroups of band_gemm_kernel.  The launch's tiles, in
-// band_gemm_kernel's grid order (row-major, longest first), go first to slot 0
-// of every workgroup, then slot 1, and so on (one tile per CU before two);
-// after its first tile a slot takes the next one from the launch's counter
-// `ctr` (zero at the start).  A slot runs each tile exactly as
+// per tile; a tile diagonal of up to 64 tiles finds them empty).  The four
+// 4-wave slots of a workgroup work independently, like four workgroups of
+// band_gemm_kernel.  The launch's tiles, in band_gemm_kernel's grid order
+// (row-major, longest first), form SIDE_QUEUES queues: queue x holds the rows
+// y = x (mod SIDE_QUEUES), row after row.  Workgroup b works on queue
+// b mod SIDE_QUEUES (linear workgroup ids reach the 8 XCDs round-robin, so a
+// queue's rows, which share their A operand blocks, stay in one XCD's L2):
+// its first tiles are dealt to slot 0 of every workgroup of that queue, then
+// slot 1, and so on; after that a slot takes the next tile of its queue from
+// the queue's counter, and once its queue is empty, from the next queues in
+// turn (counters `ctr`, zero at the start).  A slot runs each tile exactly as
 // band_gemm_kernel does, with a barrier of its own four waves (a counter in
 // LDS) in place of the workgroup barrier.  A slot barrier waits for the three
 // other waves of the slot, which run the same sequence of barriers; the wait
@@ -909,6 +923,7 @@ constexpr int SIDE_WG = 160;
 // stay at SIDE_WG (11008 x 4096: 17.8 ms with 160, 18.0 with 192).
 constexpr int SIDE_WG_QUARTER = 192;
 constexpr int SIDE_THREADS = 1024;
+constexpr int SIDE_QUEUES = 8;  // tile queues (and counters) of one side launch
 constexpr int SPIN_LIMIT = 1 << 22;
 
 __global__ __launch_bounds__(SIDE_THREADS) void band_side_kernel(BandArgs g, int *ctr,
@@ -925,7 +940,21 @@ __global__ __launch_bounds__(SIDE_THREADS) void band_side_kernel(BandArgs g, int
     const float *bp = Bs + q * TB * GP + (wc * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
     float *as_w = As + q * TB * GP + lr * GP + lc;
     float *bs_w = Bs + q * TB * GP + lr * GP + lc;
-    const int first = 4 * gridDim.x;  // tiles dealt before the counter is used
+    // queue x: rows x, x + SIDE_QUEUES, ...; its workgroups b = x (mod SIDE_QUEUES)
+    // deal its first 4 * (their number) tiles before its counter is used
+    const int x = blockIdx.x % SIDE_QUEUES, lb = blockIdx.x / SIDE_QUEUES;
+    auto qcount = [&](int qq) { return qq < g.rows ? (g.rows - qq + SIDE_QUEUES - 1) / SIDE_QUEUES * g.cols : 0; };
+    auto qfirst = [&](int qq) { return 4 * (((int)gridDim.x - qq + SIDE_QUEUES - 1) / SIDE_QUEUES); };
+    auto qtile = [&](int qq, int i) { return (qq + SIDE_QUEUES * (i / g.cols)) * g.cols + i % g.cols; };
+    auto take = [&]() {  // the next tile from the queues, from this workgroup's own on
+        for (int k = 0; k < SIDE_QUEUES; ++k) {
+            const int qq = (x + k) % SIDE_QUEUES, cnt = qcount(qq), f = qfirst(qq);
+            if (f >= cnt) continue;
+            const int i = f + atomicAdd(ctr + qq, 1);
+            if (i < cnt) return qtile(qq, i);
+        }
+        return ntile;
+    };
     if (tid < 4) s_arrive[tid] = 0;
     __syncthreads();  // the only barrier of the whole workgroup
     int target = 0, stuck = 0;
@@ -941,10 +970,18 @@ __global__ __launch_bounds__(SIDE_THREADS) void band_side_kernel(BandArgs g, int
             __builtin_amdgcn_s_sleep(1);
         }
     };
-    int t = q * gridDim.x + blockIdx.x;
+    // the slot's first tile: dealt, or (uniformly over the slot) taken from the queues
+    const int i0 = q * ((int)(gridDim.x - x + SIDE_QUEUES - 1) / SIDE_QUEUES) + lb;
+    int t = i0 < qcount(x) ? qtile(x, i0) : -1;
+    if (t < 0) {
+        if (wq == 0 && lane == 0) s_tile[q] = take();
+        slot_barrier();
+        t = s_tile[q];
+        slot_barrier();  // every wave has read s_tile[q] before it is written again
+    }
     while (t < ntile) {
         int next = 0;
-        if (wq == 0 && lane == 0) next = first + atomicAdd(ctr, 1);  // published after this tile
+        if (wq == 0 && lane == 0) next = take();  // published after this tile
         const int gy = t / g.cols, gx = t - gy * g.cols;
         const int bx = g.olo + g.cols - 1 - gx;
         const int by = (g.mode == 1 || g.mode == 3) ? g.rows - 1 - gy : gy;
@@ -1512,8 +1549,8 @@ size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     int nctr = std::max(1, shape_info(M, N).side_ops);
     if (N >= 2) nctr = std::max({nctr, shape_info(M, N / 2).side_ops, shape_info(M, N - N / 2).side_ops});
     if (M >= 2) nctr = std::max({nctr, shape_info(M / 2, N).side_ops, shape_info(M - M / 2, N).side_ops});
-    int *ctr = cv.take<int>(nctr);
-    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part, ctr, nctr};
+    int *ctr = cv.take<int>(nctr * SIDE_QUEUES);
+    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part, ctr, nctr * SIDE_QUEUES};
     return cv.used;
 }
 
@@ -1821,7 +1858,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
                 BK_MARK(1);
                 continue;
             }
-            int *ctr = op.side ? b.ctr + side_k++ : nullptr;
+            int *ctr = op.side ? b.ctr + SIDE_QUEUES * side_k++ : nullptr;
             int launched = 0;
             const int32_t st = launch_band(pv, op, ctr, op.side && side ? side : stream, &launched);
             if (st != BAKRON_OK) return st;
@@ -2008,7 +2045,7 @@ int32_t replay_band(const Solve &sv, int dev, hipStream_t stream, int side, doub
         int side_k = 0;
         for (const Op &op : plan.ops) {
             if (op.kind != OP_BAND) continue;
-            int *ctr = op.side ? sv.b.ctr + side_k++ : nullptr;
+            int *ctr = op.side ? sv.b.ctr + SIDE_QUEUES * side_k++ : nullptr;
             if (op.side != side) continue;
             int launched = 0;
             st = launch_band(sv, op, ctr, ds.cap, &launched);
