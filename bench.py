@@ -42,8 +42,10 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 # which this library's kernels do not use (scalar FMAs reach half of it)
 FP32_VALU_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
-PROFILE_MD = os.path.join(ROOT, "profiles", "band_gemm_leaf_4096x4096_int4.md")
-PROFILED_WORKLOAD = "c3"  # the workload and launch configuration the summary was taken on
+# committed rocprofv3 summaries, per workload, of this command's default launch
+# configuration (graph replay, automatic product order)
+PROFILES = {"c3": os.path.join(ROOT, "profiles", "band_gemm_leaf_4096x4096_int4.md"),
+            "c5": os.path.join(ROOT, "profiles", "band_gemm_leaf_4096x14336_int2asym.md")}
 
 
 def parse():
@@ -207,15 +209,16 @@ def main():
     leaf_gbs = leaf_bytes / sched["leaf_launches"] / leaf_avg_s / 1e9
     dominant = "band_gemm" if ph["band_ms"] >= ph["leaf_ms"] else "leaf"
     # HBM bytes per band-GEMM dispatch from the committed rocprofv3 counter
-    # summary of the 4096 x 4096 workload (this default run), null for other
-    # workloads and unless it was taken from the current kernel source
+    # summary of this workload, null for workloads without one and unless it was
+    # taken from the current kernel source
     from two_sided_gptq_amd import profsum
-    profiled = args.workload == PROFILED_WORKLOAD and args.order == 0 and not args.eager
-    traffic = profsum.read_traffic(PROFILE_MD, "band_gemm_kernel") if profiled else None
+    profile_md = PROFILES.get(args.workload)
+    profiled = profile_md is not None and args.order == 0 and not args.eager
+    traffic = profsum.read_traffic(profile_md, "band_gemm_kernel") if profiled else None
     # MFMA utilisation from the same summary's counters: fp32 MFMA flops the
     # hardware counted per dispatch (executed, so the zero halves of triangular
     # blocks included) over this run's average launch duration, against the peak
-    counted = (profsum.read_figure(PROFILE_MD, "mfma_flops_per_dispatch", "band_gemm_kernel")
+    counted = (profsum.read_figure(profile_md, "mfma_flops_per_dispatch", "band_gemm_kernel")
                if profiled else None)
     mfma_util = counted / gemm_avg_s / 1e12 / FP32_MFMA_PEAK_TFLOPS if counted and gemm_avg_s else None
     roofline = {"kernel": "band_gemm_kernel", "bound": "mfma", "achieved": gemm_tflops,

@@ -38,7 +38,7 @@ KERNEL_SOURCE = os.path.join(HERE, "csrc", "quantize.hip")
 COPY_BYTES = 1 << 30
 SIMDS = 256 * 4
 CLOCK_HZ = 2.4e9
-MFMA_KERNELS = ("band_gemm_kernel", "band_side_kernel", "leaf_kernel<false>")
+MFMA_KERNELS = ("band_gemm_kernel", "band_side_kernel", "leaf_kernel<false>", "leaf_kernel<true>")
 
 
 def source_hash(path: str = KERNEL_SOURCE) -> str:
