@@ -426,33 +426,53 @@ __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const
     }
 }
 
-// The LJ bulk dots of one helper unit over NCH 16-wide chunks of k: every
-// load is issued before the first product.  Elements at or beyond len are
-// masked (the chain may be writing them).
+// The LJ bulk dots of one helper unit over NCH 16-wide chunks of k, software
+// pipelined: chunk ch+1 is requested before chunk ch is multiplied, and a
+// scheduling barrier keeps the compiler from moving the requests of a later
+// chunk ahead of an earlier one (the LDS wait counter retires requests in
+// order, so a late-issued first chunk would stall every product behind all of
+// the unit's loads).  Elements at or beyond len are masked (the chain may be
+// writing them).
+struct UnitChunk {
+    float4 x, y[LJ];
+};
+
+__device__ __forceinline__ void unit_load(UnitChunk &c, const float *X, const float *const (&Y)[LJ],
+                                          int ch) {
+    c.x = *reinterpret_cast<const float4 *>(X + 16 * ch);
+#pragma unroll
+    for (int p = 0; p < LJ; ++p) c.y[p] = *reinterpret_cast<const float4 *>(Y[p] + 16 * ch);
+}
+
+template <bool MASK>
+__device__ __forceinline__ void unit_fma(const UnitChunk &c, int k0, int len, float (&acc)[LJ]) {
+    float4 xm = c.x;
+    if (MASK) {
+        xm.x = k0 < len ? xm.x : 0.0f;
+        xm.y = k0 + 1 < len ? xm.y : 0.0f;
+        xm.z = k0 + 2 < len ? xm.z : 0.0f;
+        xm.w = k0 + 3 < len ? xm.w : 0.0f;
+    }
+#pragma unroll
+    for (int p = 0; p < LJ; ++p) acc[p] = dot4(xm, c.y[p], acc[p]);
+}
+
 template <int NCH>
 __device__ __forceinline__ void unit_dots(const float *X, const float *const (&Y)[LJ], int len,
                                           int q, float (&acc)[LJ]) {
-    float4 x[NCH], y[NCH][LJ];
+    UnitChunk c0, c1;
+    unit_load(c0, X, Y, 0);
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        x[ch] = *reinterpret_cast<const float4 *>(X + 16 * ch);
-#pragma unroll
-        for (int p = 0; p < LJ; ++p) y[ch][p] = *reinterpret_cast<const float4 *>(Y[p] + 16 * ch);
-    }
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-        float4 xm = x[ch];
+        UnitChunk &cur = (ch & 1) ? c1 : c0;
+        UnitChunk &nxt = (ch & 1) ? c0 : c1;
+        if (ch + 1 < NCH) unit_load(nxt, X, Y, ch + 1);
+        __builtin_amdgcn_sched_barrier(0);
         // the units of a wave differ by at most 8 in length, so only its last
         // two chunks can reach beyond a unit's length
-        if (ch + 2 >= NCH) {
-            const int k0 = 16 * ch + 4 * q;
-            xm.x = k0 < len ? xm.x : 0.0f;
-            xm.y = k0 + 1 < len ? xm.y : 0.0f;
-            xm.z = k0 + 2 < len ? xm.z : 0.0f;
-            xm.w = k0 + 3 < len ? xm.w : 0.0f;
-        }
-#pragma unroll
-        for (int p = 0; p < LJ; ++p) acc[p] = dot4(xm, y[ch][p], acc[p]);
+        if (ch + 2 >= NCH) unit_fma<true>(cur, 16 * ch + 4 * q, len, acc);
+        else unit_fma<false>(cur, 16 * ch + 4 * q, len, acc);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -513,6 +533,9 @@ __device__ __forceinline__ void leaf_helpers(const int w, const int lane) {
     constexpr int kBlockOf[12] = {-1, 0, 1, 2, 6, 5, 4, 3, 7, 8, 8, 8};
     const int q = lane & 3;
     const int g = 16 * kBlockOf[w] + (lane >> 2);  // this group's unit rank (>= 128: none)
+    // kept rolled: unrolled, the sweep's code outgrows the instruction cache
+    // that two CUs share, and the chain's loop is refetched every block
+#pragma unroll 1
     for (int t = 0; t < NBLK; ++t) {
         if (t + 1 < NBLK) {
             // bulk of block t+1: diagonals D0 .. D0+LJ-1, terms of steps < s0
@@ -617,43 +640,67 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     const int64_t r0 = (int64_t)I * TB, c0 = (int64_t)J * TB;
 
     const bool pull_up = (flags & LEAF_PULL) && I >= 1, pull_left = (flags & LEAF_PULL) && J >= 1;
-    for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
+    const bool push_right = (flags & LEAF_PUSH) && J + 1 < a.N, push_down = (flags & LEAF_PUSH) && I + 1 < a.M;
+    // Every global read of the prologue is issued before the first LDS write,
+    // so the tile's loads share one memory round trip: each thread reads its
+    // float4 of every operand for at most two positions, and the row
+    // parameters.  A leaf pulls or pushes, never both, so two extra operands
+    // cover either case: x1 is Cd (pulling) or LA(J+1,J) (pushing), x2 is Cr
+    // or LB(I+1,I).  The reads are unconditional (straight-line code keeps
+    // them in flight together); an operand the leaf does not use is read from
+    // its own W tile, and its value is discarded.
+    static_assert(2 * LEAF_THREADS >= TB * 16 && LEAF_THREADS <= TB * 16, "two positions per thread");
+    float s_ld = 1.0f, z_ld = 0.0f;
+    if (tid < TB) {
+        s_ld = a.sc[r0 + tid];
+        z_ld = a.zp[r0 + tid];
+    }
+    struct PrologueLoads {
+        float4 w, lb, la, x1, x2;
+    };
+    auto load_at = [&](int idx) {
         const int r = idx >> 4, c4 = (idx & 15) * 4;
         const int64_t g = (r0 + r) * a.np + c0 + c4;
-        float4 wv = *reinterpret_cast<const float4 *>(a.Wp + g);
+        const int64_t gb = (r0 + r) * a.mp + r0 + c4, ga = (c0 + r) * a.np + c0 + c4;
+        const float *x1 = pull_up ? a.Cd + g : push_right ? a.LAp + ga + TB * a.np : a.Wp + g;
+        const float *x2 = pull_left ? a.Cr + g : push_down ? a.LBp + gb + TB * a.mp : a.Wp + g;
+        PrologueLoads l;
+        l.w = *reinterpret_cast<const float4 *>(a.Wp + g);
+        l.lb = *reinterpret_cast<const float4 *>(a.LBp + gb);
+        l.la = *reinterpret_cast<const float4 *>(a.LAp + ga);
+        l.x1 = *reinterpret_cast<const float4 *>(x1);
+        l.x2 = *reinterpret_cast<const float4 *>(x2);
+        return l;
+    };
+    auto store_at = [&](int idx, const PrologueLoads &l) {
+        const int r = idx >> 4, c4 = (idx & 15) * 4;
+        float4 wv = l.w;
         if (pull_up) {
-            const float4 d = *reinterpret_cast<const float4 *>(a.Cd + g);
-            wv.x -= d.x; wv.y -= d.y; wv.z -= d.z; wv.w -= d.w;
+            wv.x -= l.x1.x; wv.y -= l.x1.y; wv.z -= l.x1.z; wv.w -= l.x1.w;
         }
         if (pull_left) {  // V, applied in the sweep; stored skewed like W
-            const float4 v = *reinterpret_cast<const float4 *>(a.Cr + g);
             float *vk = lf_P + r * WSP + r + c4;
-            vk[0] = v.x;
-            vk[1] = v.y;
-            vk[2] = v.z;
-            vk[3] = v.w;
+            vk[0] = l.x2.x;
+            vk[1] = l.x2.y;
+            vk[2] = l.x2.z;
+            vk[3] = l.x2.w;
         }
         float *wk = lf_Wk + r * WSP + r + c4;
         wk[0] = wv.x;
         wk[1] = wv.y;
         wk[2] = wv.z;
         wk[3] = wv.w;
-        *reinterpret_cast<float4 *>(lf_B + r * LP + c4) =
-            *reinterpret_cast<const float4 *>(a.LBp + (r0 + r) * a.mp + r0 + c4);
-        *reinterpret_cast<float4 *>(lf_A + r * LP + c4) =
-            *reinterpret_cast<const float4 *>(a.LAp + (c0 + r) * a.np + c0 + c4);
-    }
-    if (flags & LEAF_PUSH) {
-        for (int idx = tid; idx < TB * 16; idx += LEAF_THREADS) {
-            const int r = idx >> 4, c4 = (idx & 15) * 4;
-            if (J + 1 < a.N)
-                *reinterpret_cast<float4 *>(lf_P + r * GP + c4) =
-                    *reinterpret_cast<const float4 *>(a.LAp + (c0 + TB + r) * a.np + c0 + c4);
-            if (I + 1 < a.M)
-                *reinterpret_cast<float4 *>(lf_P + (TB + r) * GP + c4) =
-                    *reinterpret_cast<const float4 *>(a.LBp + (r0 + TB + r) * a.mp + r0 + c4);
-        }
-    }
+        *reinterpret_cast<float4 *>(lf_B + r * LP + c4) = l.lb;
+        *reinterpret_cast<float4 *>(lf_A + r * LP + c4) = l.la;
+        if (push_right) *reinterpret_cast<float4 *>(lf_P + r * GP + c4) = l.x1;
+        if (push_down) *reinterpret_cast<float4 *>(lf_P + (TB + r) * GP + c4) = l.x2;
+    };
+    const bool second = tid < TB * 16 - LEAF_THREADS;
+    const PrologueLoads l0 = load_at(tid);
+    PrologueLoads l1;
+    if (second) l1 = load_at(tid + LEAF_THREADS);
+    store_at(tid, l0);
+    if (second) store_at(tid + LEAF_THREADS, l1);
     for (int idx = tid; idx < 2 * 2 * TB * LJ / 4; idx += LEAF_THREADS)
         reinterpret_cast<float4 *>(lf_bulk)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (pull_left) {  // the skewed V's slots outside a row's 64 entries
@@ -663,10 +710,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
         }
     }
     __syncthreads();
-    if (tid < TB) {
-        const float s = a.sc[r0 + tid];
-        lf_row[tid] = make_float4(s, 1.0f / s, a.zp[r0 + tid], 1.0f / lf_B[tid * LP + tid]);
-    }
+    if (tid < TB) lf_row[tid] = make_float4(s_ld, 1.0f / s_ld, z_ld, 1.0f / lf_B[tid * LP + tid]);
     for (int x = tid; x < NCX; x += LEAF_THREADS) {
         const int c = x - CX;
         float band[8];
