@@ -28,7 +28,7 @@ namespace {
 
 constexpr int FT = 64;
 constexpr int FP = 65;   // LDS row stride (doubles) of the base block
-constexpr int GK = 16;   // k chunk of the products
+constexpr int GK = 32;   // k chunk of the products
 constexpr int GS = GK + 1;
 
 typedef double doublex4 __attribute__((ext_vector_type(4)));
@@ -229,27 +229,44 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DGemm g) {
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = doublex4{0.0, 0.0, 0.0, 0.0};
-    const double *Ab = g.A + (int64_t)FT * ib * g.lda;
+    // Each thread moves 8 consecutive doubles of A and of B per k chunk: A and
+    // (bnn = 0) B by row (row t / 4, k offset 8 (t % 4)); B (bnn = 1) by k row
+    // (t / 8, columns 8 (t % 8) ..).  The next chunk is read into registers
+    // while the current one is multiplied.
+    const int row = t >> 2, kk = (t & 3) * 8;
+    const int kr = t >> 3, jj = (t & 7) * 8;
+    const double *Asrc = g.A + ((int64_t)FT * ib + row) * g.lda + kk;
+    const double *Bsrc = g.bnn ? g.B + (int64_t)kr * g.ldb + (int64_t)FT * jb + jj
+                               : g.B + ((int64_t)FT * jb + row) * g.ldb + kk;
+    const int64_t bstep = g.bnn ? (int64_t)g.ldb : 1;  // B address advance per unit of k
+    double ra[8], rb[8];
+    if (klo < khi) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            ra[q] = Asrc[klo + q];
+            rb[q] = Bsrc[klo * bstep + q];
+        }
+    }
     for (int k0 = klo; k0 < khi; k0 += GK) {
         __syncthreads();
-        {   // A: 64 rows x 16 k, 4 consecutive k per thread
-            const int row = t >> 2, kk = (t & 3) * 4;
-            const double *src = Ab + (int64_t)row * g.lda + k0 + kk;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) As[row * GS + kk + q] = src[q];
-        }
+        for (int q = 0; q < 8; ++q) As[row * GS + kk + q] = ra[q];
         if (!g.bnn) {
-            const int row = t >> 2, kk = (t & 3) * 4;
-            const double *src = g.B + ((int64_t)FT * jb + row) * g.ldb + k0 + kk;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) Bs[row * GS + kk + q] = src[q];
+            for (int q = 0; q < 8; ++q) Bs[row * GS + kk + q] = rb[q];
         } else {
-            const int kk = t >> 4, j = (t & 15) * 4;
-            const double *src = g.B + (int64_t)(k0 + kk) * g.ldb + (int64_t)FT * jb + j;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) Bs[(j + q) * GS + kk] = src[q];
+            for (int q = 0; q < 8; ++q) Bs[(jj + q) * GS + kr] = rb[q];
         }
         __syncthreads();
+        if (k0 + GK < khi) {
+            const int kn = k0 + GK;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                ra[q] = Asrc[kn + q];
+                rb[q] = Bsrc[kn * bstep + q];
+            }
+        }
         // lane l supplies A[l % 16][k] and B[k][l % 16] with k = 4 s + l / 16
 #pragma unroll
         for (int s = 0; s < GK / 4; ++s) {
