@@ -257,18 +257,13 @@ __device__ inline float dot4(const float4 a, const float4 b, float s) {
 // The chain and the helpers meet at a workgroup barrier once every LJ steps:
 // during block t (steps LJ t .. LJ t + LJ - 1) the helpers compute the bulk
 // of block t+1 from the E and Z values of steps < LJ t, which the previous
-// barrier made visible, into the other half of a double buffer.  A helper
-// unit is one row r (row-direction bulk of its LJ entries in the block, which
-// share E[r][0..]) or one column c (column-direction bulk of its LJ entries,
-// which share Z[0..][c]); 4 lanes split each dot into float4 chunks and a DPP
-// butterfly sums them.  Values the chain may be writing concurrently are never
-// used: the operand is masked to the bulk's length before multiplying.
+// barrier made visible, into the other half of a double buffer (the helper
+// units are described at leaf_helpers).
 constexpr int LJ = 4;                               // chain steps per block
 constexpr int LWIN = 2 * LJ - 1;                    // most recent terms per dot
 constexpr int NBLK = (2 * TB - 1 + LJ - 1) / LJ;    // blocks covering the sweep
 constexpr int NSTEP = NBLK * LJ;                    // steps including the idle tail
 constexpr int LEAF_THREADS = 768;                   // 12 waves, three per SIMD (wave w on SIMD w % 4)
-static_assert(16 * 8 == 2 * TB, "at most 8 blocks of 16 helper units");
 constexpr int WSP = NSTEP + 4;                      // row stride of the skewed W copy
 constexpr int CX = TB;                              // index of column 0 in the padded LA tables
 constexpr int NCX = CX + NSTEP + 4;                 // padded LA table length (columns -64 .. 131)
@@ -426,132 +421,105 @@ __device__ __forceinline__ void leaf_chain(const int r, const float qminf, const
     }
 }
 
-// The LJ bulk dots of one helper unit over NCH 16-wide chunks of k, software
-// pipelined: chunk ch+1 is requested before chunk ch is multiplied, and a
-// scheduling barrier keeps the compiler from moving the requests of a later
-// chunk ahead of an earlier one (the LDS wait counter retires requests in
-// order, so a late-issued first chunk would stall every product behind all of
-// the unit's loads).  Elements at or beyond len are masked (the chain may be
-// writing them).
-struct UnitChunk {
-    float4 x, y[LJ];
-};
-
-__device__ __forceinline__ void unit_load(UnitChunk &c, const float *X, const float *const (&Y)[LJ],
-                                          int ch) {
-    c.x = *reinterpret_cast<const float4 *>(X + 16 * ch);
-#pragma unroll
-    for (int p = 0; p < LJ; ++p) c.y[p] = *reinterpret_cast<const float4 *>(Y[p] + 16 * ch);
-}
-
-template <bool MASK>
-__device__ __forceinline__ void unit_fma(const UnitChunk &c, int k0, int len, float (&acc)[LJ]) {
-    float4 xm = c.x;
-    if (MASK) {
-        xm.x = k0 < len ? xm.x : 0.0f;
-        xm.y = k0 + 1 < len ? xm.y : 0.0f;
-        xm.z = k0 + 2 < len ? xm.z : 0.0f;
-        xm.w = k0 + 3 < len ? xm.w : 0.0f;
-    }
-#pragma unroll
-    for (int p = 0; p < LJ; ++p) acc[p] = dot4(xm, c.y[p], acc[p]);
-}
-
+// Helper units stay in their factor rows.  A row-direction unit with anchor a
+// takes, in the block whose first diagonal is D0, the LJ entries (x, a + p) of
+// row x = D0 - a; their bulk runs over k < s0 - x = a - LJ against the rows
+// LA[a + p][.].  x and D0 advance together, so the unit meets the same four
+// factor rows and the same length in every block: it reads them once, into
+// registers, with the entries at k >= a - LJ (and rows past the tile) set to
+// zero, and per block reads only its E row.  A column-direction unit takes
+// the entries (a + p, x) of column x = D0 - a, against LB[a + p][.] and the
+// column Z[.][x] (row x of lf_Z).  The zeroed factor entries make masks
+// unnecessary: E and Z are zeroed before the sweep, so an entry the chain may
+// be writing during the block is zero or final, and it meets a zero factor
+// entry either way.  Anchors a <= LJ have no bulk terms; their bulk slots keep
+// the zeros they start with.
+//
+// A unit is 4 lanes; lane q takes k = 16 ch + 4 q .. + 3 of each 16-wide
+// chunk ch, and a 4 x 4 DPP transpose-reduce leaves it entry q's total.  The
+// units of one wave share a direction and a chunk count NCH: anchors
+// 16 (NCH - 1) + 5 .. 16 NCH + 4, so one wave per (direction, NCH).  Within a
+// block, chunk ch+1 is requested before chunk ch is multiplied (a scheduling
+// barrier keeps that order: the LDS wait counter retires requests in order).
 template <int NCH>
-__device__ __forceinline__ void unit_dots(const float *X, const float *const (&Y)[LJ], int len,
-                                          int q, float (&acc)[LJ]) {
-    UnitChunk c0, c1;
-    unit_load(c0, X, Y, 0);
+__device__ __forceinline__ void helper_sweep(const int dir, const int a, const int q) {
+    const bool unit = a <= TB - 1;
+    const int len = a - LJ;
+    const float *F = dir ? lf_B : lf_A;
+    float4 y[NCH][LJ];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-        UnitChunk &cur = (ch & 1) ? c1 : c0;
-        UnitChunk &nxt = (ch & 1) ? c0 : c1;
-        if (ch + 1 < NCH) unit_load(nxt, X, Y, ch + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        // the units of a wave differ by at most 8 in length, so only its last
-        // two chunks can reach beyond a unit's length
-        if (ch + 2 >= NCH) unit_fma<true>(cur, 16 * ch + 4 * q, len, acc);
-        else unit_fma<false>(cur, 16 * ch + 4 * q, len, acc);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// Helper units come in groups of four: (row or column idx, idx + 1) x (row
-// direction, column direction).  The two units in one 8-lane half of a group
-// share the direction, so their operand rows (idx and idx + 1, 80 floats
-// apart) fall in different LDS banks; units of the two directions at one idx
-// read arrays that start in the same bank.
-__device__ __forceinline__ int unit_idx(int u) { return 2 * (u >> 2) + (u & 1); }
-__device__ __forceinline__ int unit_dir(int u) { return (u >> 1) & 1; }
-
-// One helper unit: 4 lanes (q = 0..3) compute the LJ bulk dots of one row
-// (dir 0, row direction, X = E[idx][.], Y = LA rows of the entries' columns) or
-// one column (dir 1, column direction, X = Z[.][idx], Y = LB rows of the
-// entries' rows) over k < len; lane q then holds entry q's total and writes it.
-// nch (at least ceil(len / 16)) is uniform over the wave.
-__device__ __forceinline__ void helper_unit(int u, int lo, int D0, int s0, float *buf, int q,
-                                            int nch) {
-    const int idx = lo + unit_idx(u), dir = unit_dir(u);
-    const int len = s0 - idx;
-    const float *X = (dir ? lf_Z : lf_E) + idx * LP + 4 * q;
-    const float *Yb = (dir ? lf_B : lf_A) + 4 * q;
-    const float *Y[LJ];
-    float acc[LJ];
+    for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
-    for (int p = 0; p < LJ; ++p) {
-        Y[p] = Yb + clamp_col(D0 + p - idx) * LP;
-        acc[p] = 0.0f;
-    }
-    switch (nch) {
-        case 1: unit_dots<1>(X, Y, len, q, acc); break;
-        case 2: unit_dots<2>(X, Y, len, q, acc); break;
-        case 3: unit_dots<3>(X, Y, len, q, acc); break;
-        case 4: unit_dots<4>(X, Y, len, q, acc); break;
-        default: break;
-    }
-    // 4 x 4 transpose-reduce over the group: lane q ends with entry q's sum
+        for (int p = 0; p < LJ; ++p) {
+            const int k0 = 16 * ch + 4 * q, row = min(a + p, TB - 1);
+            float4 v = *reinterpret_cast<const float4 *>(F + row * LP + k0);
+            const bool in = unit && a + p <= TB - 1;
+            v.x = in && k0 < len ? v.x : 0.0f;
+            v.y = in && k0 + 1 < len ? v.y : 0.0f;
+            v.z = in && k0 + 2 < len ? v.z : 0.0f;
+            v.w = in && k0 + 3 < len ? v.w : 0.0f;
+            y[ch][p] = v;
+        }
+    const float *Xb = (dir ? lf_Z : lf_E) + 4 * q;
     const bool o1 = q & 1, o2 = q & 2;
-    const float k0v = o1 ? acc[1] : acc[0], s0v = o1 ? acc[0] : acc[1];
-    const float k1v = o1 ? acc[3] : acc[2], s1v = o1 ? acc[2] : acc[3];
-    const float r0 = k0v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0v), 0xB1, 0xF, 0xF, false));
-    const float r1 = k1v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1v), 0xB1, 0xF, 0xF, false));
-    const float kv = o2 ? r1 : r0, sv = o2 ? r0 : r1;
-    const float tot = kv + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sv), 0x4E, 0xF, 0xF, false));
-    const int other = D0 + q - idx;
-    float *dst = (other >= 0 && other < TB) ? buf + (dir * TB + (dir ? other : idx)) * LJ + q
-                                            : lf_sink + 2 * TB + (threadIdx.x & 63);
-    *dst = tot;
-}
-
-// helper waves w = 1..11, lane groups of 4.  Units are taken in order of
-// decreasing length, 16 to a wave (at most 8 such blocks).  The six longest
-// blocks go in pairs to SIMDs 1-3 (blocks 0 + 5, 1 + 4, 2 + 3: equal chunk
-// counts when all 8 are in use), the two shortest to the waves that share
-// the chain's SIMD (4 and 8), which otherwise idle; waves 9-11 get none.
-// The chain's instruction rate is unchanged by them (measured).
-__device__ __forceinline__ void leaf_helpers(const int w, const int lane) {
-    constexpr int kBlockOf[12] = {-1, 0, 1, 2, 6, 5, 4, 3, 7, 8, 8, 8};
-    const int q = lane & 3;
-    const int g = 16 * kBlockOf[w] + (lane >> 2);  // this group's unit rank (>= 128: none)
     // kept rolled: unrolled, the sweep's code outgrows the instruction cache
     // that two CUs share, and the chain's loop is refetched every block
 #pragma unroll 1
     for (int t = 0; t < NBLK; ++t) {
-        if (t + 1 < NBLK) {
-            // bulk of block t+1: diagonals D0 .. D0+LJ-1, terms of steps < s0
-            const int D0 = LJ * (t + 1), s0 = LJ * t;
-            const int lo = max(0, D0 - (TB - 1)), hi = min(TB - 1, D0 + LJ - 1);
-            const int nrow = hi - lo + 1;
-            const int nunit = 4 * ((nrow + 1) >> 1);
+        const int x = LJ * (t + 1) - a;  // this block's row (column) of the unit
+        if (t + 1 < NBLK && unit && x >= 0 && x < TB) {
+            const float *X = Xb + x * LP;
+            float acc[LJ];
+#pragma unroll
+            for (int p = 0; p < LJ; ++p) acc[p] = 0.0f;
+            float4 xc[2];
+            xc[0] = *reinterpret_cast<const float4 *>(X);
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
+                if (ch + 1 < NCH) xc[(ch + 1) & 1] = *reinterpret_cast<const float4 *>(X + 16 * (ch + 1));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int p = 0; p < LJ; ++p) acc[p] = dot4(xc[ch & 1], y[ch][p], acc[p]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // 4 x 4 transpose-reduce over the unit: lane q ends with entry q's sum
+            const float k0v = o1 ? acc[1] : acc[0], s0v = o1 ? acc[0] : acc[1];
+            const float k1v = o1 ? acc[3] : acc[2], s1v = o1 ? acc[2] : acc[3];
+            const float r0 = k0v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0v), 0xB1, 0xF, 0xF, false));
+            const float r1 = k1v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1v), 0xB1, 0xF, 0xF, false));
+            const float kv = o2 ? r1 : r0, sv = o2 ? r0 : r1;
+            const float tot = kv + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(sv), 0x4E, 0xF, 0xF, false));
+            // entry q: (x, a + q) or (a + q, x); bulk slot [dir][its row][q]
             float *buf = lf_bulk + ((t + 1) & 1) * 2 * TB * LJ;
-            // lane 0 of the wave holds its longest unit, whose chunk count every
-            // group of the wave uses
-            const int g0 = __builtin_amdgcn_readfirstlane(g);
-            const int len0 = s0 - (lo + unit_idx(g0));
-            const int nch = len0 > 0 ? (len0 + 15) >> 4 : 0;
-            if (g < nunit && unit_idx(g) < nrow) helper_unit(g, lo, D0, s0, buf, q, nch);
+            float *dst = a + q <= TB - 1 ? buf + (dir * TB + (dir ? a + q : x)) * LJ + q
+                                         : lf_sink + 2 * TB + (threadIdx.x & 63);
+            *dst = tot;
         }
         __syncthreads();
+    }
+}
+
+// helper waves w = 1..11 (wave w on SIMD w % 4; SIMD 0 also runs the chain):
+// the two four-chunk classes on SIMDs 1 and 2, each beside a two-chunk class,
+// the two three-chunk classes on SIMD 3, the one-chunk classes beside the
+// chain; waves 9-11 only meet the barriers.
+__device__ __forceinline__ void leaf_helpers(const int w, const int lane) {
+    // (NCH - 1) * 2 + direction, or -1
+    constexpr int kClass[12] = {-1, 6, 7, 4, 0, 2, 3, 5, 1, -1, -1, -1};
+    const int cls = kClass[w];
+    const int q = lane & 3;
+    if (cls < 0) {
+#pragma unroll 1
+        for (int t = 0; t < NBLK; ++t) __syncthreads();
+        return;
+    }
+    const int nch = (cls >> 1) + 1, dir = cls & 1;
+    const int a = 16 * (nch - 1) + LJ + 1 + (lane >> 2);
+    switch (nch) {
+        case 1: helper_sweep<1>(dir, a, q); break;
+        case 2: helper_sweep<2>(dir, a, q); break;
+        case 3: helper_sweep<3>(dir, a, q); break;
+        default: helper_sweep<4>(dir, a, q); break;
     }
 }
 
@@ -703,6 +671,11 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     if (second) store_at(tid + LEAF_THREADS, l1);
     for (int idx = tid; idx < 2 * 2 * TB * LJ / 4; idx += LEAF_THREADS)
         reinterpret_cast<float4 *>(lf_bulk)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // E and Z start at zero: the helpers read entries the chain has not written yet
+    for (int idx = tid; idx < TB * LP / 4; idx += LEAF_THREADS) {
+        reinterpret_cast<float4 *>(lf_E)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+        reinterpret_cast<float4 *>(lf_Z)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     if (pull_left) {  // the skewed V's slots outside a row's 64 entries
         for (int idx = tid; idx < TB * (WSP - TB); idx += LEAF_THREADS) {
             const int r = idx / (WSP - TB), k = idx - r * (WSP - TB);
