@@ -379,8 +379,6 @@ __device__ __forceinline__ void chain_block(ChainState &st, const ChainBlock &cb
         code[p] = qz;
         *(act ? lf_E + st.e_off + d : lf_sink + r) = e;
         *(act ? lf_Z + st.z_off + d * LP : lf_sink + TB + r) = z;
-        e = act ? e : 0.0f;
-        z = act ? z : 0.0f;
 #pragma unroll
         for (int j = LWIN - 1; j >= 1; --j) {
             st.eh[j] = st.eh[j - 1];
@@ -676,11 +674,13 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
         reinterpret_cast<float4 *>(lf_E)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
         reinterpret_cast<float4 *>(lf_Z)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (pull_left) {  // the skewed V's slots outside a row's 64 entries
-        for (int idx = tid; idx < TB * (WSP - TB); idx += LEAF_THREADS) {
-            const int r = idx / (WSP - TB), k = idx - r * (WSP - TB);
-            lf_P[r * WSP + (k < r ? k : k + TB)] = 0.0f;
-        }
+    // the skewed W's (and V's) slots outside a row's 64 entries: zero, so an
+    // off-tile step's pre-rounding value is finite and its error, scaled by the
+    // zero reciprocal of an off-tile column, exactly zero
+    for (int idx = tid; idx < TB * (WSP - TB); idx += LEAF_THREADS) {
+        const int r = idx / (WSP - TB), k = idx - r * (WSP - TB);
+        lf_Wk[r * WSP + (k < r ? k : k + TB)] = 0.0f;
+        if (pull_left) lf_P[r * WSP + (k < r ? k : k + TB)] = 0.0f;
     }
     __syncthreads();
     if (tid < TB) lf_row[tid] = make_float4(s_ld, 1.0f / s_ld, z_ld, 1.0f / lf_B[tid * LP + tid]);
