@@ -665,23 +665,35 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     const PrologueLoads l0 = load_at(tid);
     PrologueLoads l1;
     if (second) l1 = load_at(tid + LEAF_THREADS);
-    store_at(tid, l0);
-    if (second) store_at(tid + LEAF_THREADS, l1);
+    // while the loads are in flight: the LDS that starts at zero
     for (int idx = tid; idx < 2 * 2 * TB * LJ / 4; idx += LEAF_THREADS)
         reinterpret_cast<float4 *>(lf_bulk)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
-    // E and Z start at zero: the helpers read entries the chain has not written yet
+    // E and Z: the helpers read entries the chain has not written yet
     for (int idx = tid; idx < TB * LP / 4; idx += LEAF_THREADS) {
         reinterpret_cast<float4 *>(lf_E)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
         reinterpret_cast<float4 *>(lf_Z)[idx] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    // the skewed W's (and V's) slots outside a row's 64 entries: zero, so an
+    // the skewed W's (and V's) slots outside a row's 64 entries, so that an
     // off-tile step's pre-rounding value is finite and its error, scaled by the
-    // zero reciprocal of an off-tile column, exactly zero
-    for (int idx = tid; idx < TB * (WSP - TB); idx += LEAF_THREADS) {
-        const int r = idx / (WSP - TB), k = idx - r * (WSP - TB);
-        lf_Wk[r * WSP + (k < r ? k : k + TB)] = 0.0f;
-        if (pull_left) lf_P[r * WSP + (k < r ? k : k + TB)] = 0.0f;
-    }
+    // zero reciprocal of an off-tile column, exactly zero: the 16 positions
+    // (r, 4 j) of row r take its WSP - TB such slots k = j, j + 16, ...
+    static_assert(WSP - TB <= 5 * 16, "five pad slots per position");
+    auto zero_pad = [&](int idx) {
+        const int r = idx >> 4, j = idx & 15;
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const int k = j + 16 * m;
+            if (k < WSP - TB) {
+                const int slot = r * WSP + (k < r ? k : k + TB);
+                lf_Wk[slot] = 0.0f;
+                if (pull_left) lf_P[slot] = 0.0f;
+            }
+        }
+    };
+    zero_pad(tid);
+    if (second) zero_pad(tid + LEAF_THREADS);
+    store_at(tid, l0);
+    if (second) store_at(tid + LEAF_THREADS, l1);
     __syncthreads();
     if (tid < TB) lf_row[tid] = make_float4(s_ld, 1.0f / s_ld, z_ld, 1.0f / lf_B[tid * LP + tid]);
     for (int x = tid; x < NCX; x += LEAF_THREADS) {
