@@ -29,6 +29,7 @@ namespace {
 constexpr int FT = 64;
 constexpr int FP = 65;   // LDS row stride (doubles) of the base block
 constexpr int GK = 32;   // k chunk of the products
+constexpr int DB = 16;   // diagonal sub-block of the base
 constexpr int GS = GK + 1;
 
 typedef double doublex4 __attribute__((ext_vector_type(4)));
@@ -64,126 +65,211 @@ __device__ __forceinline__ double rsqrt_nr(double x) {
     return y;
 }
 
+__device__ __forceinline__ double readlane_d(const double x, const int lane) {
+    const long long b = __double_as_longlong(x);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)b, lane);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(b >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// keeps the wave's LDS accesses in program order (the hardware runs one
+// wave's LDS operations in order)
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+// One 16 x 16 x 16 product on the matrix cores, one wave:
+// acc += sa * A B with A[r][k] = pa[r * lda + k], B[k][c] = pb[k * sbk + c * sbc].
+// Lane l supplies A[l % 16][k] and B[k][l % 16] for k = 4 s + l / 16; register
+// v of lane l holds the output entry (l / 16 + 4 v, l % 16).
+__device__ __forceinline__ void mm16(doublex4 &acc, const double *pa, const int lda, const double *pb,
+                                     const int sbk, const int sbc, const double sa, const int l) {
+    const int r = l & 15, kq = l >> 4;
+    double av[4], bv[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        av[s] = sa * pa[r * lda + 4 * s + kq];
+        bv[s] = pb[(4 * s + kq) * sbk + r * sbc];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[s], bv[s], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ doublex4 ld16(const double *p, const int l) {
+    doublex4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = p[((l >> 4) + 4 * k) * FP + (l & 15)];
+    return v;
+}
+
+__device__ __forceinline__ void st16(double *p, const int l, const doublex4 v) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[((l >> 4) + 4 * k) * FP + (l & 15)] = v[k];
+}
+
+// The 16 x 16 diagonal block at (o, o) of sA: its Cholesky factor in place and
+// the inverse of that factor into sX, by one wave, right-looking and
+// interleaved as for a whole block, with the column exchange through a
+// wave-local LDS area (no barrier).  Lane l = 4 i + q holds A[i][4 v + q] and
+// S[i][4 v + q] (v = 0..3).  At column j:
+//   the pivot's 1 / sqrt r and value come from lane 4 j + j % 4 (readlane);
+//   the owners of column j publish P_i = A_ij for rows i > j and zero for rows
+//   <= j, and row j's lanes publish S'_jc = S_jc (c < j), -1 (c = j), 0 (c > j),
+//   both at position (k % 4) * 4 + k / 4 so each lane reads its four columns
+//   as one contiguous run;
+//   every entry takes A_ik -= w_i P_k and S_ik -= w_i S'_jk with w_i = P_i r^2
+//   (so rows <= j and columns <= j of A stay as they are); column j's owners
+//   scale it, C_ij = A_ij r (i > j).
+// Afterwards sA holds C below the diagonal and the last pivots A_ii on it, and
+// sX holds X_ic = -S_ic r_i (c < i), r_i (c = i), zero above.
+__device__ __forceinline__ void diag16(double *sA, double *sX, double *dC, double *dS, const int o,
+                                       const int l, int &bad) {
+    const int i = l >> 2, q = l & 3;
+    double a[4], s[4], e[4], ri = 0.0;  // e: the identity's entries, ri: r of this lane's row
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        a[v] = sA[(o + i) * FP + o + 4 * v + q];
+        s[v] = 0.0;
+        e[v] = 4 * v + q == i ? 1.0 : 0.0;
+    }
+    double rn = rsqrt_nr(a[0]);  // every lane's own entry; lane 4 j + j % 4 holds the pivot's
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+        const int jv = j >> 2, qj = j & 3, pl = 4 * j + qj;
+        double r = readlane_d(rn, pl);
+        const double piv = readlane_d(a[jv], pl);
+        if (!(piv > 0.0) || !isfinite(piv)) {
+            bad = 1;
+            r = rsqrt_nr(1.0);
+        }
+        // j as an opaque per-column value: the lane masks are then formed here
+        // instead of all being hoisted ahead of the loop (which spills them)
+        int jo;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(jo) : "i"(j));
+        ri = i == jo ? r : ri;
+        // lanes that publish nothing write their own spare slot, so there is no branch
+        dC[q == qj ? (i & 3) * 4 + (i >> 2) : DB + l] = i > jo ? a[jv] : 0.0;
+        {   // row j: S_jc is zero for c > j (those entries are never updated), so
+            // S'_j = S_j - e_j
+            double2 *ds = reinterpret_cast<double2 *>(i == jo ? dS + 4 * q : dS + DB + 4 * l);
+            ds[0] = double2{s[0] - e[0], s[1] - e[1]};
+            ds[1] = double2{s[2] - e[2], s[3] - e[3]};
+        }
+        lds_order();
+        const double pr = dC[(i & 3) * 4 + (i >> 2)];
+        const double2 c0 = reinterpret_cast<const double2 *>(dC + 4 * q)[0];
+        const double2 c1 = reinterpret_cast<const double2 *>(dC + 4 * q)[1];
+        const double2 x0 = reinterpret_cast<const double2 *>(dS + 4 * q)[0];
+        const double2 x1 = reinterpret_cast<const double2 *>(dS + 4 * q)[1];
+        lds_order();
+        const double cv[4] = {c0.x, c0.y, c1.x, c1.y}, xv[4] = {x0.x, x0.y, x1.x, x1.y};
+        const double w = pr * r * r;
+        if (j + 1 < DB) {  // the next pivot's entry first, so its 1 / sqrt overlaps the rest
+            const int nv = (j + 1) >> 2;
+            a[nv] = fma(-w, cv[nv], a[nv]);
+            rn = rsqrt_nr(a[nv]);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            if (j + 1 >= DB || v != ((j + 1) >> 2)) a[v] = fma(-w, cv[v], a[v]);
+            s[v] = fma(-w, xv[v], s[v]);
+        }
+        if (q == qj) a[jv] = i > jo ? a[jv] * r : a[jv];
+    }
+    lds_order();
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int c = 4 * v + q;
+        sA[(o + i) * FP + o + c] = a[v];
+        sX[(o + i) * FP + o + c] = c < i ? -s[v] * ri : (c == i ? ri : 0.0);
+    }
+}
+
 // One 64 x 64 diagonal block at (off, off): its Cholesky factor and the
-// inverse of that factor, right-looking and interleaved, one workgroup.
-// Thread (i, q) = (t / 4, t % 4) owns the entries of row i in the columns
-// k = q (mod 4), 16 of A (the trailing matrix, then C) and 16 of S (pending
-// sums of X = C^-1).  Columns go in groups jb of four; during group jb the
-// thread holds, in registers with fixed indices,
-//   ar[m'] = A[i][4 (jb + m') + q]   (m' = 0..15; zero past the block)
-//   sr[m'] = S[i][4 (jb - m') + q]   (m' = 0..15; zero before the block)
-// and between groups both windows move by one (the finished A entry ar[0]
-// goes to the LDS staging copy of the block).  At column j = 4 jb + qj:
-//   publish  r = 1 / sqrt(A_jj) (from the diagonal's owner), the column
-//            A[k][j] unscaled (from its owners, rows k > j), and the pending
-//            row S[j][c] with -1 at c = j (from row j's threads)
-//   barrier
-//   update   the column's owners scale C_ij = A_ij r; every row i > j, with
-//            w = A_ij r^2: A_ik -= w A_kj (k > j), i.e. C_ij C_kj, and
-//            S_ic -= w S'_jc (c <= j), i.e. + C_ij X_jc with X_jc = -S_jc r
-//            (c < j), X_jj = r; row j's threads keep r_j.
-// Row j of X is X_jc = -S_jc r_j (c < j), X_jj = r_j, formed when the block is
-// written out.  Rows i <= j take w = 0, which leaves them unchanged.  The
-// published rows sit in LDS rows of 32 with zero padding on the side the
-// windows run past, so only the entries of the current group need a mask.
-// Two LDS sets alternate by column parity, so one barrier per column
-// separates every write from the reads of the same set.  The block is staged
-// through LDS on the way in and out, so the global accesses are coalesced.
+// inverse of that factor, one workgroup, blocked by 16.  For the diagonal
+// blocks p = 0..3 in turn (sA holds A, then C; sX the block sums S, then X):
+//   (a) one wave factors and inverts the diagonal block (diag16);
+//   (b) C_ip = A_ip X_pp^T (i > p) and X_pc = -X_pp S_pc (c < p);
+//   (c) A_ik -= C_ip C_kp^T (p < k <= i) and S_ic += C_ip X_pc (i > p, c <= p);
+// (b) and (c) are 16 x 16 x 16 products on the fp64 matrix cores, spread over
+// the four waves, with a barrier after each phase.  This is the block form of
+// the same recursion (C X = I by block forward substitution, S_pc the sum over
+// m < p of C_pm X_mc).  The block goes in and out through LDS, so the global
+// accesses are coalesced.
+__device__ __forceinline__ void base_block(const double *G, double *C, double *X, int64_t dp, int64_t off,
+                                           int &bad) {
+    __shared__ double sA[FT * FP];
+    __shared__ double sX[FT * FP];
+    __shared__ __align__(16) double dC[DB + 64];      // the column, then one spare slot per lane
+    __shared__ __align__(16) double dS[DB + 4 * 64];  // the pending row, then four spare slots per lane
+    const int t = threadIdx.x, w = t >> 6, l = t & 63;
+    for (int idx = t; idx < FT * FT; idx += 256) {
+        const int i = idx >> 6, k = idx & 63;
+        sA[i * FP + k] = G[(off + i) * dp + off + k];
+        sX[i * FP + k] = 0.0;
+    }
+    __syncthreads();
+    if (w == 0) diag16(sA, sX, dC, dS, 0, l, bad);
+    for (int p = 0; p < FT / DB; ++p) {
+        const int o = DB * p;
+        __syncthreads();
+        // (b): 3 products, one per wave 1..3: C_ip for i = p+1..3, then X_pc for c = 0..p-1
+        if (w > 0) {
+            const int e = w - 1, nc = 3 - p;
+            doublex4 acc{0.0, 0.0, 0.0, 0.0};
+            if (e < nc) {
+                const int i = p + 1 + e;
+                mm16(acc, &sA[DB * i * FP + o], FP, &sX[o * FP + o], 1, FP, 1.0, l);
+                st16(&sA[DB * i * FP + o], l, acc);
+            } else {
+                const int c = e - nc;
+                mm16(acc, &sX[o * FP + o], FP, &sX[o * FP + DB * c], FP, 1, -1.0, l);
+                st16(&sX[o * FP + DB * c], l, acc);
+            }
+        }
+        __syncthreads();
+        // (c): wave 0 updates the next diagonal block and factors it at once, while
+        // waves 1..3 take the other trailing blocks round-robin
+        if (w == 0) {
+            if (p + 1 < FT / DB) {
+                const int i = p + 1;
+                doublex4 acc = ld16(&sA[DB * i * FP + DB * i], l);
+                mm16(acc, &sA[DB * i * FP + o], FP, &sA[DB * i * FP + o], 1, FP, -1.0, l);
+                st16(&sA[DB * i * FP + DB * i], l, acc);
+                lds_order();
+                diag16(sA, sX, dC, dS, DB * i, l, bad);
+            }
+        } else {
+            int n = 0;
+            for (int i = p + 1; i < FT / DB; ++i)
+                for (int k = p + 1; k <= i; ++k) {
+                    if (i == p + 1 && k == p + 1) continue;
+                    if (n++ % 3 == w - 1) {
+                        doublex4 acc = ld16(&sA[DB * i * FP + DB * k], l);
+                        mm16(acc, &sA[DB * i * FP + o], FP, &sA[DB * k * FP + o], 1, FP, -1.0, l);
+                        st16(&sA[DB * i * FP + DB * k], l, acc);
+                    }
+                }
+            for (int i = p + 1; i < FT / DB; ++i)
+                for (int c = 0; c <= p; ++c)
+                    if (n++ % 3 == w - 1) {
+                        doublex4 acc = ld16(&sX[DB * i * FP + DB * c], l);
+                        mm16(acc, &sA[DB * i * FP + o], FP, &sX[o * FP + DB * c], FP, 1, 1.0, l);
+                        st16(&sX[DB * i * FP + DB * c], l, acc);
+                    }
+        }
+    }
+    __syncthreads();
+    for (int idx = t; idx < FT * FT; idx += 256) {
+        const int i = idx >> 6, k = idx & 63;
+        const double v = sA[i * FP + k];
+        C[(off + i) * dp + off + k] = k < i ? v : (k == i ? sqrt(v) : 0.0);
+        X[(off + i) * dp + off + k] = k <= i ? sX[i * FP + k] : 0.0;
+    }
+}
+
 __global__ __launch_bounds__(256) void base_kernel(const double *__restrict__ G, double *C, double *X,
                                                    int64_t dp, int64_t off, int32_t *dev_status) {
-    constexpr int NM = FT / 4;
-    __shared__ double st[FT * FP];          // staging of the block
-    // rows of 34 doubles, so the four rows a wave reads start 16 bytes apart in the banks
-    constexpr int RW = 2 * NM + 2;
-    __shared__ double s_col[2][4][RW];  // [parity][k % 4][k / 4], zero at k / 4 >= 16
-    __shared__ double s_xs[2][4][RW];   // [parity][c % 4][16 + c / 4], zero below 16
-    __shared__ double s_rc[2];
-    const int t = threadIdx.x, ri = t >> 2, q = t & 3;
-    for (int idx = t; idx < FT * FT; idx += 256) {
-        const int i = idx >> 6, k = idx & 63;
-        st[i * FP + k] = k <= i ? G[(off + i) * dp + off + k] : 0.0;
-    }
-    for (int idx = t; idx < 2 * 4 * RW; idx += 256) {
-        (&s_col[0][0][0])[idx] = 0.0;
-        (&s_xs[0][0][0])[idx] = 0.0;
-    }
-    __syncthreads();
-    double ar[NM], sr[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        ar[m] = st[ri * FP + 4 * m + q];
-        sr[m] = 0.0;
-    }
     int bad = 0;
-    double rrow = 0.0;  // r_i of this thread's row, once column i is done
-    for (int jb = 0; jb < NM; ++jb) {
-        if (jb > 0) {
-            st[ri * FP + 4 * (jb - 1) + q] = ar[0];
-#pragma unroll
-            for (int m = 0; m + 1 < NM; ++m) ar[m] = ar[m + 1];
-            ar[NM - 1] = 0.0;
-#pragma unroll
-            for (int m = NM - 1; m > 0; --m) sr[m] = sr[m - 1];
-            sr[0] = 0.0;
-        }
-#pragma unroll
-        for (int qj = 0; qj < 4; ++qj) {
-            const int j = 4 * jb + qj, par = qj & 1;
-            // publish
-            if (ri == j && q == qj) {
-                double ajj = ar[0];
-                if (!(ajj > 0.0) || !isfinite(ajj)) {
-                    bad = 1;
-                    ajj = 1.0;
-                }
-                s_rc[par] = rsqrt_nr(ajj);
-            }
-            if (q == qj && ri > j) s_col[par][ri & 3][ri >> 2] = ar[0];
-            if (ri == j) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m)
-                    s_xs[par][q][NM + jb - m] = (m == 0 && q == qj) ? -1.0 : sr[m];
-            }
-            __syncthreads();
-            // update
-            const double rc = s_rc[par];
-            rrow = ri == j ? rc : rrow;
-            const double w = ri > j ? s_col[par][ri & 3][ri >> 2] * rc * rc : 0.0;
-            const double *cq = &s_col[par][q][jb];
-            const double *xq = &s_xs[par][q][NM + jb];
-            {   // the current group: column 4 jb + q is past j for q > qj, j itself for q = qj
-                const double v = fma(-w, cq[0], ar[0]);
-                const double sc = ri > j ? ar[0] * rc : ar[0];
-                ar[0] = q > qj ? v : (q == qj ? sc : ar[0]);
-                const double u = fma(-w, xq[0], sr[0]);
-                sr[0] = q <= qj ? u : sr[0];
-            }
-#pragma unroll
-            for (int m = 1; m < NM; ++m) {
-                ar[m] = fma(-w, cq[m], ar[m]);
-                sr[m] = fma(-w, xq[-m], sr[m]);
-            }
-        }
-    }
-    // C (upper part zero, diagonal sqrt of the last A_ii) and X through LDS
-    st[ri * FP + 4 * (NM - 1) + q] = ar[0];
-    __syncthreads();
-    for (int idx = t; idx < FT * FT; idx += 256) {
-        const int i = idx >> 6, k = idx & 63;
-        const double v = st[i * FP + k];
-        C[(off + i) * dp + off + k] = k < i ? v : (k == i ? sqrt(v) : 0.0);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        const int k = 4 * (NM - 1 - m) + q;
-        st[ri * FP + k] = k < ri ? -sr[m] * rrow : (k == ri ? rrow : 0.0);
-    }
-    __syncthreads();
-    for (int idx = t; idx < FT * FT; idx += 256) {
-        const int i = idx >> 6, k = idx & 63;
-        X[(off + i) * dp + off + k] = st[i * FP + k];
-    }
+    base_block(G, C, X, dp, off, bad);
     if (bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
 }
 
@@ -203,6 +289,99 @@ struct DGemm {
     double alpha, beta;
 };
 
+// The output tile (ib, jb) of TM x TM of one product, by one workgroup of 256
+// threads: each wave takes a TM/2 x TM/2 quarter as (TM/32)^2 blocks of 16 x 16
+// on the matrix cores.  Every output entry sums its k in the same order and in
+// the same groups of four whatever TM is, so the tile size does not change the
+// result; the skipped k blocks hold exact zeros.
+template <int TM>
+__device__ __forceinline__ void dgemm_tile(const DGemm &g, const int ib, const int jb) {
+    constexpr int WT = TM / 2, NB = WT / 16;
+    constexpr int LPT = TM * GK / 256;  // doubles of A (and of B) each thread moves per k chunk
+    constexpr int TPR = GK / LPT;       // threads per row of A (and of B by row)
+    constexpr int TPK = TM / LPT;       // threads per k row of B (bnn = 1)
+    int klo = 0, khi = g.K;
+    if (g.kmode == 1) khi = min(g.K, TM * (ib + 1));
+    if (g.kmode == 2) khi = min(g.K, TM * (jb + 1));
+    if (g.kmode == 3) klo = TM * jb;
+    __shared__ double As[TM * GS];
+    __shared__ double Bs[TM * GS];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int qr = w >> 1, qc = w & 1;
+    doublex4 acc[NB][NB];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[a][b] = doublex4{0.0, 0.0, 0.0, 0.0};
+    // Each thread moves LPT consecutive doubles of A and of B per k chunk: A and
+    // (bnn = 0) B by row (row t / TPR, k offset LPT (t % TPR)); B (bnn = 1) by k
+    // row (t / TPK, columns LPT (t % TPK) ..).  The next chunk is read into
+    // registers while the current one is multiplied.
+    const int row = t / TPR, kk = (t % TPR) * LPT;
+    const int kr = t / TPK, jj = (t % TPK) * LPT;
+    const double *Asrc = g.A + ((int64_t)TM * ib + row) * g.lda + kk;
+    const double *Bsrc = g.bnn ? g.B + (int64_t)kr * g.ldb + (int64_t)TM * jb + jj
+                               : g.B + ((int64_t)TM * jb + row) * g.ldb + kk;
+    const int64_t bstep = g.bnn ? (int64_t)g.ldb : 1;  // B address advance per unit of k
+    double ra[LPT], rb[LPT];
+    if (klo < khi) {
+#pragma unroll
+        for (int q = 0; q < LPT; ++q) {
+            ra[q] = Asrc[klo + q];
+            rb[q] = Bsrc[klo * bstep + q];
+        }
+    }
+    for (int k0 = klo; k0 < khi; k0 += GK) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < LPT; ++q) As[row * GS + kk + q] = ra[q];
+        if (!g.bnn) {
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) Bs[row * GS + kk + q] = rb[q];
+        } else {
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) Bs[(jj + q) * GS + kr] = rb[q];
+        }
+        __syncthreads();
+        if (k0 + GK < khi) {
+            const int kn = k0 + GK;
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) {
+                ra[q] = Asrc[kn + q];
+                rb[q] = Bsrc[kn * bstep + q];
+            }
+        }
+        // lane l supplies A[l % 16][k] and B[k][l % 16] with k = 4 s + l / 16
+#pragma unroll
+        for (int s = 0; s < GK / 4; ++s) {
+            double av[NB], bv[NB];
+#pragma unroll
+            for (int a = 0; a < NB; ++a) av[a] = As[(WT * qr + 16 * a + (lane & 15)) * GS + 4 * s + (lane >> 4)];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) bv[b] = Bs[(WT * qc + 16 * b + (lane & 15)) * GS + 4 * s + (lane >> 4)];
+#pragma unroll
+            for (int a = 0; a < NB; ++a)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+    }
+    // register v of lane l holds D[l / 16 + 4 v][l % 16] of each 16 x 16 block
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = (int64_t)TM * ib + WT * qr + 16 * a + (lane >> 4) + 4 * v;
+                const int64_t col = (int64_t)TM * jb + WT * qc + 16 * b + (lane & 15);
+                double *c = g.C + row * g.ldc + col;
+                const double r = g.alpha * acc[a][b][v];
+                *c = g.beta != 0.0 ? fma(g.beta, *c, r) : r;
+            }
+}
+
+template <int TM>
 __global__ __launch_bounds__(256) void dgemm_kernel(DGemm g) {
     int ib, jb;
     if (g.lower) {
@@ -216,85 +395,38 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DGemm g) {
         ib = blockIdx.y;
         jb = blockIdx.x;
     }
-    int klo = 0, khi = g.K;
-    if (g.kmode == 1) khi = min(g.K, FT * (ib + 1));
-    if (g.kmode == 2) khi = min(g.K, FT * (jb + 1));
-    if (g.kmode == 3) klo = FT * jb;
-    __shared__ double As[FT * GS];
-    __shared__ double Bs[FT * GS];
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int qr = w >> 1, qc = w & 1;
-    doublex4 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = doublex4{0.0, 0.0, 0.0, 0.0};
-    // Each thread moves 8 consecutive doubles of A and of B per k chunk: A and
-    // (bnn = 0) B by row (row t / 4, k offset 8 (t % 4)); B (bnn = 1) by k row
-    // (t / 8, columns 8 (t % 8) ..).  The next chunk is read into registers
-    // while the current one is multiplied.
-    const int row = t >> 2, kk = (t & 3) * 8;
-    const int kr = t >> 3, jj = (t & 7) * 8;
-    const double *Asrc = g.A + ((int64_t)FT * ib + row) * g.lda + kk;
-    const double *Bsrc = g.bnn ? g.B + (int64_t)kr * g.ldb + (int64_t)FT * jb + jj
-                               : g.B + ((int64_t)FT * jb + row) * g.ldb + kk;
-    const int64_t bstep = g.bnn ? (int64_t)g.ldb : 1;  // B address advance per unit of k
-    double ra[8], rb[8];
-    if (klo < khi) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            ra[q] = Asrc[klo + q];
-            rb[q] = Bsrc[klo * bstep + q];
-        }
-    }
-    for (int k0 = klo; k0 < khi; k0 += GK) {
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 8; ++q) As[row * GS + kk + q] = ra[q];
-        if (!g.bnn) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) Bs[row * GS + kk + q] = rb[q];
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) Bs[(jj + q) * GS + kr] = rb[q];
-        }
-        __syncthreads();
-        if (k0 + GK < khi) {
-            const int kn = k0 + GK;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                ra[q] = Asrc[kn + q];
-                rb[q] = Bsrc[kn * bstep + q];
-            }
-        }
-        // lane l supplies A[l % 16][k] and B[k][l % 16] with k = 4 s + l / 16
-#pragma unroll
-        for (int s = 0; s < GK / 4; ++s) {
-            double av[2], bv[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) av[a] = As[(32 * qr + 16 * a + (lane & 15)) * GS + 4 * s + (lane >> 4)];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) bv[b] = Bs[(32 * qc + 16 * b + (lane & 15)) * GS + 4 * s + (lane >> 4)];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
-        }
-    }
-    // register v of lane l holds D[l / 16 + 4 v][l % 16] of each 16 x 16 block
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t row = (int64_t)FT * ib + 32 * qr + 16 * a + (lane >> 4) + 4 * v;
-                const int64_t col = (int64_t)FT * jb + 32 * qc + 16 * b + (lane & 15);
-                double *c = g.C + row * g.ldc + col;
-                const double r = g.alpha * acc[a][b][v];
-                *c = g.beta != 0.0 ? fma(g.beta, *c, r) : r;
-            }
+    dgemm_tile<TM>(g, ib, jb);
+}
+
+// A whole 128 x 128 recursion node at (off, off) in one workgroup: the two
+// diagonal blocks and the four one-tile products between them, in the order
+// and with the arithmetic of the separate launches (so the result is the
+// same), without five launches in between.  The workgroup's global writes are
+// visible to its own later reads after each barrier.
+__global__ __launch_bounds__(256) void node128_kernel(double *G, double *C, double *X, double *T,
+                                                      int64_t dp, int64_t off, int32_t *dev_status) {
+    auto at = [dp](double *p, int64_t r, int64_t c) { return p + r * dp + c; };
+    const int64_t o2 = off + FT;
+    int bad = 0;
+    base_block(G, C, X, dp, off, bad);
+    __syncthreads();
+    // C21 = G21 X11^T
+    dgemm_tile<FT>(DGemm{at(G, o2, off), dp, at(X, off, off), dp, at(C, o2, off), dp, FT, FT, FT, 0, 2, 0, 1.0, 0.0},
+               0, 0);
+    __syncthreads();
+    // G22 -= C21 C21^T
+    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(C, o2, off), dp, at(G, o2, o2), dp, FT, FT, FT, 0, 0, 1, -1.0, 1.0},
+               0, 0);
+    __syncthreads();
+    base_block(G, C, X, dp, o2, bad);
+    __syncthreads();
+    // T = C21 X11, X21 = -X22 T
+    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(X, off, off), dp, at(T, o2, off), dp, FT, FT, FT, 1, 3, 0, 1.0, 0.0},
+               0, 0);
+    __syncthreads();
+    dgemm_tile<FT>(DGemm{at(X, o2, o2), dp, at(T, o2, off), dp, at(X, o2, off), dp, FT, FT, FT, 1, 1, 0, -1.0, 0.0},
+               0, 0);
+    if (bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
 }
 
 // L[a][b] = X[d-1-b][d-1-a] for b <= a, 0 above; tiled transpose through LDS
@@ -339,15 +471,33 @@ struct Factor {
     hipStream_t stream;
 };
 
+template <int TM>
+void launch_gemm(const DGemm &g, const int M, const int N, const hipStream_t stream) {
+    const int mb = M / TM, nb = N / TM;
+    if (g.lower) {
+        hipLaunchKernelGGL(dgemm_kernel<TM>, dim3((unsigned)(mb * (mb + 1) / 2)), dim3(256), 0, stream, g);
+    } else {
+        hipLaunchKernelGGL(dgemm_kernel<TM>, dim3(nb, mb), dim3(256), 0, stream, g);
+    }
+}
+
+// The tile size: 64 if that still gives at least one workgroup per compute
+// unit, else 32 (an fp64 tile runs at one compute unit's matrix rate, so small
+// products need small tiles).  Tiles stay at most 64 wide: the k range a
+// triangular operand skips is cut at the tile's own rows or columns, and only
+// the diagonal 64 x 64 blocks of C and X have their upper part written (as
+// zeros), so a wider tile would read blocks above the diagonal that are never
+// written.
+int gemm_tile(const int M, const int N, const int lower) {
+    const int64_t mb = M / FT, nb = N / FT;
+    return (lower ? mb * (mb + 1) / 2 : mb * nb) >= 256 ? FT : 32;
+}
+
 int32_t gemm(const Factor &fc, const double *A, const double *B, double *Cout, int M, int N, int K,
              int bnn, int kmode, int lower, double alpha, double beta) {
-    DGemm g{A, fc.dp, B, fc.dp, Cout, fc.dp, M, N, K, bnn, kmode, lower, alpha, beta};
-    const int mb = M / FT, nb = N / FT;
-    if (lower) {
-        hipLaunchKernelGGL(dgemm_kernel, dim3((unsigned)(mb * (mb + 1) / 2)), dim3(256), 0, fc.stream, g);
-    } else {
-        hipLaunchKernelGGL(dgemm_kernel, dim3(nb, mb), dim3(256), 0, fc.stream, g);
-    }
+    const DGemm g{A, fc.dp, B, fc.dp, Cout, fc.dp, M, N, K, bnn, kmode, lower, alpha, beta};
+    if (gemm_tile(M, N, lower) == FT) launch_gemm<FT>(g, M, N, fc.stream);
+    else launch_gemm<32>(g, M, N, fc.stream);
     BK_LAUNCH_CHECK("dgemm_kernel");
     return BAKRON_OK;
 }
@@ -359,6 +509,12 @@ int32_t recurse(const Factor &fc, int64_t off, int64_t n) {
         hipLaunchKernelGGL(base_kernel, dim3(1), dim3(256), 0, fc.stream, fc.f.G, fc.f.C, fc.f.X, dp,
                            off, fc.dev_status);
         BK_LAUNCH_CHECK("base_kernel");
+        return BAKRON_OK;
+    }
+    if (n == 2 * FT) {
+        hipLaunchKernelGGL(node128_kernel, dim3(1), dim3(256), 0, fc.stream, fc.f.G, fc.f.C, fc.f.X,
+                           fc.f.T, dp, off, fc.dev_status);
+        BK_LAUNCH_CHECK("node128_kernel");
         return BAKRON_OK;
     }
     const int64_t n1 = (n / FT / 2) * FT, n2 = n - n1;
