@@ -122,3 +122,30 @@ def test_hessian_and_factor_at_config_size(bk):
           f"max |L^T H L - I| {np.max(np.abs(R)):.3e}")
     assert ferr < 1e-6
     assert np.max(np.abs(R)) < 1e-4
+
+
+def test_factor_side_stream_matches_one_stream(bk):
+    """At d >= 2048 the wide recursion nodes' T = C21 X11 products run on a side
+    stream beside the recursion into G22, joined before X21 = -X22 T; a call
+    captured into a graph keeps every step on the capturing stream.  Both give
+    the same L bit for bit (the products' arithmetic does not depend on the
+    stream), on the 4096-wide input Hessian of the 4096 x 4096 workload and on
+    the 2048-wide leading block of it; so does a repeated eager call."""
+    w = synth.WORKLOADS["c3"]
+    H = bk.hessian(torch.from_numpy(synth.input_samples(w)).cuda(), synth.DAMP)
+    for Hd in (H, H[:2048, :2048].contiguous()):
+        L1 = bk.factor(Hd)
+        L2 = bk.factor(Hd)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            bk.factor(Hd)  # warm-up on the capturing stream
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            L3 = bk.factor(Hd)
+        for _ in range(2):
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(L1, L3)
+        assert torch.equal(L1, L2)

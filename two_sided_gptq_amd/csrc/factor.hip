@@ -19,6 +19,8 @@
 // block held in registers (base_kernel).  The products run on fp64 MFMA
 // (v_mfma_f64_16x16x4f64) in 64 x 64 output tiles, skipping the k blocks where
 // a triangular operand is zero.
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "common.hpp"
@@ -287,6 +289,7 @@ struct DGemm {
     int64_t ldc;
     int M, N, K, bnn, kmode, lower;
     double alpha, beta;
+    int xcd;  // a 1-D grid whose workgroup x takes the output rows ib = x (mod 8) (mb % 8 = 0)
 };
 
 // The output tile (ib, jb) of TM x TM of one product, by one workgroup of 256
@@ -391,6 +394,12 @@ __global__ __launch_bounds__(256) void dgemm_kernel(DGemm g) {
         while ((a + 1) * (a + 2) / 2 <= x) ++a;
         ib = (int)a;
         jb = (int)(x - a * (a + 1) / 2);
+    } else if (g.xcd) {
+        // linear workgroup ids reach the 8 XCDs round-robin: XCD x takes the rows
+        // ib = x (mod 8), a whole row at a time, so a row's A panel is read into one L2
+        const int nb = g.N / TM, x = blockIdx.x & 7, k = blockIdx.x >> 3;
+        ib = x + 8 * (k / nb);
+        jb = k % nb;
     } else {
         ib = blockIdx.y;
         jb = blockIdx.x;
@@ -411,20 +420,20 @@ __global__ __launch_bounds__(256) void node128_kernel(double *G, double *C, doub
     base_block(G, C, X, dp, off, bad);
     __syncthreads();
     // C21 = G21 X11^T
-    dgemm_tile<FT>(DGemm{at(G, o2, off), dp, at(X, off, off), dp, at(C, o2, off), dp, FT, FT, FT, 0, 2, 0, 1.0, 0.0},
+    dgemm_tile<FT>(DGemm{at(G, o2, off), dp, at(X, off, off), dp, at(C, o2, off), dp, FT, FT, FT, 0, 2, 0, 1.0, 0.0, 0},
                0, 0);
     __syncthreads();
     // G22 -= C21 C21^T
-    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(C, o2, off), dp, at(G, o2, o2), dp, FT, FT, FT, 0, 0, 1, -1.0, 1.0},
+    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(C, o2, off), dp, at(G, o2, o2), dp, FT, FT, FT, 0, 0, 1, -1.0, 1.0, 0},
                0, 0);
     __syncthreads();
     base_block(G, C, X, dp, o2, bad);
     __syncthreads();
     // T = C21 X11, X21 = -X22 T
-    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(X, off, off), dp, at(T, o2, off), dp, FT, FT, FT, 1, 3, 0, 1.0, 0.0},
+    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(X, off, off), dp, at(T, o2, off), dp, FT, FT, FT, 1, 3, 0, 1.0, 0.0, 0},
                0, 0);
     __syncthreads();
-    dgemm_tile<FT>(DGemm{at(X, o2, o2), dp, at(T, o2, off), dp, at(X, o2, off), dp, FT, FT, FT, 1, 1, 0, -1.0, 0.0},
+    dgemm_tile<FT>(DGemm{at(X, o2, o2), dp, at(T, o2, off), dp, at(X, o2, off), dp, FT, FT, FT, 1, 1, 0, -1.0, 0.0, 0},
                0, 0);
     if (bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
 }
@@ -464,18 +473,40 @@ size_t fcarve(void *ws, int64_t dp, FBufs *f) {
     return cv.used;
 }
 
+// Nodes at least this wide run T = C21 X11 on a side stream, beside the
+// recursion into G22 (T needs only C21 and X11; the recursion is latency-bound
+// and leaves most of the GPU idle), and join it before X21 = -X22 T.
+constexpr int64_t SIDE_T_MIN = 1024;
+
+// Per device: the side stream and a pool of fork / join events, used under
+// one lock for the whole enqueue of a factor call.
+struct FactorSide {
+    hipStream_t side = nullptr;
+    std::vector<hipEvent_t> ev;
+};
+std::mutex g_fside_mu;
+std::map<int, FactorSide> g_fside;
+
 struct Factor {
     FBufs f;
     int64_t dp;
     int32_t *dev_status;
     hipStream_t stream;
+    hipStream_t side;  // nullptr: every step on stream
+    FactorSide *fs;
+    mutable int nev;   // events of fs taken so far
 };
 
+// XCD-aware tile order for wide outputs (measured: 2.6 % faster at d = 14336,
+// where the top products are 112 tiles wide; no gain at 32 tiles wide).
 template <int TM>
-void launch_gemm(const DGemm &g, const int M, const int N, const hipStream_t stream) {
+void launch_gemm(DGemm g, const int M, const int N, const hipStream_t stream) {
     const int mb = M / TM, nb = N / TM;
     if (g.lower) {
         hipLaunchKernelGGL(dgemm_kernel<TM>, dim3((unsigned)(mb * (mb + 1) / 2)), dim3(256), 0, stream, g);
+    } else if (mb % 8 == 0 && nb >= 64) {
+        g.xcd = 1;
+        hipLaunchKernelGGL(dgemm_kernel<TM>, dim3((unsigned)(mb * nb)), dim3(256), 0, stream, g);
     } else {
         hipLaunchKernelGGL(dgemm_kernel<TM>, dim3(nb, mb), dim3(256), 0, stream, g);
     }
@@ -494,11 +525,22 @@ int gemm_tile(const int M, const int N, const int lower) {
 }
 
 int32_t gemm(const Factor &fc, const double *A, const double *B, double *Cout, int M, int N, int K,
-             int bnn, int kmode, int lower, double alpha, double beta) {
-    const DGemm g{A, fc.dp, B, fc.dp, Cout, fc.dp, M, N, K, bnn, kmode, lower, alpha, beta};
-    if (gemm_tile(M, N, lower) == FT) launch_gemm<FT>(g, M, N, fc.stream);
-    else launch_gemm<32>(g, M, N, fc.stream);
+             int bnn, int kmode, int lower, double alpha, double beta, hipStream_t stream = nullptr) {
+    const DGemm g{A, fc.dp, B, fc.dp, Cout, fc.dp, M, N, K, bnn, kmode, lower, alpha, beta, 0};
+    if (!stream) stream = fc.stream;
+    if (gemm_tile(M, N, lower) == FT) launch_gemm<FT>(g, M, N, stream);
+    else launch_gemm<32>(g, M, N, stream);
     BK_LAUNCH_CHECK("dgemm_kernel");
+    return BAKRON_OK;
+}
+
+int32_t take_event(const Factor &fc, hipEvent_t *e) {
+    if (fc.nev == (int)fc.fs->ev.size()) {
+        hipEvent_t n;
+        BK_HIP_CHECK(hipEventCreateWithFlags(&n, hipEventDisableTiming));
+        fc.fs->ev.push_back(n);
+    }
+    *e = fc.fs->ev[fc.nev++];
     return BAKRON_OK;
 }
 
@@ -526,16 +568,29 @@ int32_t recurse(const Factor &fc, int64_t off, int64_t n) {
     st = gemm(fc, at(G, off + n1, off), at(X, off, off), at(C, off + n1, off), (int)n2, (int)n1,
               (int)n1, 0, 2, 0, 1.0, 0.0);
     if (st != BAKRON_OK) return st;
+    // T = C21 X11 (X11 lower: rows k >= the output column block): on the side
+    // stream for wide nodes (its region of T is this node's alone)
+    const bool side = fc.side && n >= SIDE_T_MIN;
+    hipEvent_t fork = nullptr, join = nullptr;
+    if (side) {
+        st = take_event(fc, &fork);
+        if (st == BAKRON_OK) st = take_event(fc, &join);
+        if (st != BAKRON_OK) return st;
+        BK_HIP_CHECK(hipEventRecord(fork, fc.stream));
+        BK_HIP_CHECK(hipStreamWaitEvent(fc.side, fork, 0));
+    }
+    st = gemm(fc, at(C, off + n1, off), at(X, off, off), at(T, off + n1, off), (int)n2, (int)n1,
+              (int)n1, 1, 3, 0, 1.0, 0.0, side ? fc.side : fc.stream);
+    if (st != BAKRON_OK) return st;
+    if (side) BK_HIP_CHECK(hipEventRecord(join, fc.side));
     // G22 -= C21 C21^T, lower tiles
     st = gemm(fc, at(C, off + n1, off), at(C, off + n1, off), at(G, off + n1, off + n1), (int)n2,
               (int)n2, (int)n1, 0, 0, 1, -1.0, 1.0);
     if (st != BAKRON_OK) return st;
     st = recurse(fc, off + n1, n2);
     if (st != BAKRON_OK) return st;
-    // T = C21 X11 (X11 lower: rows k >= the output column block), X21 = -X22 T (X22 lower)
-    st = gemm(fc, at(C, off + n1, off), at(X, off, off), at(T, off + n1, off), (int)n2, (int)n1,
-              (int)n1, 1, 3, 0, 1.0, 0.0);
-    if (st != BAKRON_OK) return st;
+    // X21 = -X22 T (X22 lower)
+    if (side) BK_HIP_CHECK(hipStreamWaitEvent(fc.stream, join, 0));
     st = gemm(fc, at(X, off + n1, off + n1), at(T, off + n1, off), at(X, off + n1, off), (int)n2,
               (int)n1, (int)n2, 1, 1, 0, -1.0, 0.0);
     return st;
@@ -569,7 +624,24 @@ extern "C" int32_t bakron_factor(const float *H, int64_t d, float *L, int32_t *d
     fc.dp = round_up(d, FT);
     fc.dev_status = dev_status;
     fc.stream = stream;
+    fc.side = nullptr;
+    fc.fs = nullptr;
+    fc.nev = 0;
     fcarve(ws, fc.dp, &fc.f);
+    // The side stream is shared by the device's factor calls, so a call being
+    // captured into a graph keeps every step on its own stream.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    BK_HIP_CHECK(hipStreamIsCapturing(stream, &cap));
+    int dev = 0;
+    BK_HIP_CHECK(hipGetDevice(&dev));
+    std::unique_lock<std::mutex> lock(g_fside_mu, std::defer_lock);
+    if (cap == hipStreamCaptureStatusNone && fc.dp >= 2 * SIDE_T_MIN) {
+        lock.lock();
+        FactorSide &fs = g_fside[dev];
+        if (!fs.side) BK_HIP_CHECK(hipStreamCreateWithFlags(&fs.side, hipStreamNonBlocking));
+        fc.side = fs.side;
+        fc.fs = &fs;
+    }
     hipLaunchKernelGGL(load_reversed_kernel, dim3(2048), dim3(256), 0, stream, H, d, fc.f.G, fc.dp);
     BK_LAUNCH_CHECK("load_reversed_kernel");
     st = recurse(fc, 0, fc.dp);
