@@ -80,6 +80,22 @@ def _table(out, win, title):
     out.append("")
 
 
+def _factor_windows(rows):
+    """The factor calls in a benchmark trace: each runs from its
+    load_reversed_kernel to its write_l_kernel (the side stream's products fall
+    inside that span).  The benchmark calls the input side's factor twice (one
+    warm-up, one timed), then the output side's."""
+    rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
+    wins, start = [], None
+    for i, r in enumerate(rows):
+        if "load_reversed_kernel" in r["Kernel_Name"]:
+            start = i
+        elif "write_l_kernel" in r["Kernel_Name"] and start is not None:
+            wins.append(rows[start:i + 1])
+            start = None
+    return wins
+
+
 def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str,
               mfma_command: str = "") -> str:
     out = []
@@ -90,6 +106,9 @@ def summarise(trace_dir: str, pmc_dir: str, command: str, pmc_command: str,
     _table(out, timing_win, "Timing pass (the same plan in order on one stream, an event after every step)")
     if replay_win:
         _table(out, replay_win, "Band replays (critical, then deferred launches alone; bench.py's band averages)")
+    fwins = _factor_windows(rows)
+    if len(fwins) >= 2:
+        _table(out, fwins[1], "One bakron_factor call (the input side's timed call; T products on a side stream)")
     out.append("\n### rocprofv3 --stats (whole command)\n")
     out.append("| kernel | calls | average ns | % |")
     out.append("|---|---|---|---|")
