@@ -15,10 +15,11 @@
 //   G22 -= C21 C21^T                 (lower tiles only)
 //   (C22, X22) = recurse(G22)
 //   X21  = -X22 (C21 X11)
-// down to 64 x 64 blocks, which one workgroup factors and inverts with the
-// block held in registers (base_kernel).  The products run on fp64 MFMA
-// (v_mfma_f64_16x16x4f64) in 64 x 64 output tiles, skipping the k blocks where
-// a triangular operand is zero.
+// A 128 x 128 node runs whole in one workgroup (node128_kernel); its 64 x 64
+// diagonal blocks are factored and inverted blocked by 16 (base_block).  The
+// products run on fp64 MFMA (v_mfma_f64_16x16x4f64) in 64 x 64 or 32 x 32
+// output tiles, skipping the k blocks where a triangular operand is zero; the
+// wide nodes' T = C21 X11 runs on a side stream beside the recursion into G22.
 #include <map>
 #include <mutex>
 #include <vector>
@@ -192,7 +193,10 @@ __device__ __forceinline__ void diag16(double *sA, double *sX, double *dC, doubl
 //   (b) C_ip = A_ip X_pp^T (i > p) and X_pc = -X_pp S_pc (c < p);
 //   (c) A_ik -= C_ip C_kp^T (p < k <= i) and S_ic += C_ip X_pc (i > p, c <= p);
 // (b) and (c) are 16 x 16 x 16 products on the fp64 matrix cores, spread over
-// the four waves, with a barrier after each phase.  This is the block form of
+// the four waves, with a barrier before each phase.  In (c), wave 0 updates
+// the next diagonal block first and factors it at once (its (a)), while waves
+// 1..3 finish the other trailing blocks, which that block does not read.  This
+// is the block form of
 // the same recursion (C X = I by block forward substitution, S_pc the sum over
 // m < p of C_pm X_mc).  The block goes in and out through LDS, so the global
 // accesses are coalesced.
