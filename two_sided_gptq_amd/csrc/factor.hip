@@ -31,9 +31,7 @@ namespace {
 
 constexpr int FT = 64;
 constexpr int FP = 65;   // LDS row stride (doubles) of the base block
-constexpr int GK = 32;   // k chunk of the products
 constexpr int DB = 16;   // diagonal sub-block of the base
-constexpr int GS = GK + 1;
 
 typedef double doublex4 __attribute__((ext_vector_type(4)));
 
@@ -200,8 +198,7 @@ __device__ __forceinline__ void diag16(double *sA, double *sX, double *dC, doubl
 // the same recursion (C X = I by block forward substitution, S_pc the sum over
 // m < p of C_pm X_mc).  The block goes in and out through LDS, so the global
 // accesses are coalesced.
-__device__ __forceinline__ void base_block(const double *G, double *C, double *X, int64_t dp, int64_t off,
-                                           int &bad) {
+__device__ __forceinline__ void base_block(const double *G, double *X, int64_t dp, int64_t off, int &bad) {
     __shared__ double sA[FT * FP];
     __shared__ double sX[FT * FP];
     __shared__ __align__(16) double dC[DB + 64];      // the column, then one spare slot per lane
@@ -266,16 +263,14 @@ __device__ __forceinline__ void base_block(const double *G, double *C, double *X
     __syncthreads();
     for (int idx = t; idx < FT * FT; idx += 256) {
         const int i = idx >> 6, k = idx & 63;
-        const double v = sA[i * FP + k];
-        C[(off + i) * dp + off + k] = k < i ? v : (k == i ? sqrt(v) : 0.0);
         X[(off + i) * dp + off + k] = k <= i ? sX[i * FP + k] : 0.0;
     }
 }
 
-__global__ __launch_bounds__(256) void base_kernel(const double *__restrict__ G, double *C, double *X,
-                                                   int64_t dp, int64_t off, int32_t *dev_status) {
+__global__ __launch_bounds__(256) void base_kernel(const double *__restrict__ G, double *X, int64_t dp,
+                                                   int64_t off, int32_t *dev_status) {
     int bad = 0;
-    base_block(G, C, X, dp, off, bad);
+    base_block(G, X, dp, off, bad);
     if (bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
 }
 
@@ -301,8 +296,9 @@ struct DGemm {
 // on the matrix cores.  Every output entry sums its k in the same order and in
 // the same groups of four whatever TM is, so the tile size does not change the
 // result; the skipped k blocks hold exact zeros.
-template <int TM>
+template <int TM, int GK = 32>
 __device__ __forceinline__ void dgemm_tile(const DGemm &g, const int ib, const int jb) {
+    constexpr int GS = GK + 1;  // LDS row stride (doubles)
     constexpr int WT = TM / 2, NB = WT / 16;
     constexpr int LPT = TM * GK / 256;  // doubles of A (and of B) each thread moves per k chunk
     constexpr int TPR = GK / LPT;       // threads per row of A (and of B by row)
@@ -330,6 +326,20 @@ __device__ __forceinline__ void dgemm_tile(const DGemm &g, const int ib, const i
     const double *Bsrc = g.bnn ? g.B + (int64_t)kr * g.ldb + (int64_t)TM * jb + jj
                                : g.B + ((int64_t)TM * jb + row) * g.ldb + kk;
     const int64_t bstep = g.bnn ? (int64_t)g.ldb : 1;  // B address advance per unit of k
+    // the old values of an updated tile, read now so their latency overlaps the loop
+    double cold[NB][NB][4];
+    if (g.beta != 0.0) {
+#pragma unroll
+        for (int a = 0; a < NB; ++a)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t row = (int64_t)TM * ib + WT * qr + 16 * a + (lane >> 4) + 4 * v;
+                    const int64_t col = (int64_t)TM * jb + WT * qc + 16 * b + (lane & 15);
+                    cold[a][b][v] = g.C[row * g.ldc + col];
+                }
+    }
     double ra[LPT], rb[LPT];
     if (klo < khi) {
 #pragma unroll
@@ -382,9 +392,8 @@ __device__ __forceinline__ void dgemm_tile(const DGemm &g, const int ib, const i
             for (int v = 0; v < 4; ++v) {
                 const int64_t row = (int64_t)TM * ib + WT * qr + 16 * a + (lane >> 4) + 4 * v;
                 const int64_t col = (int64_t)TM * jb + WT * qc + 16 * b + (lane & 15);
-                double *c = g.C + row * g.ldc + col;
                 const double r = g.alpha * acc[a][b][v];
-                *c = g.beta != 0.0 ? fma(g.beta, *c, r) : r;
+                g.C[row * g.ldc + col] = g.beta != 0.0 ? fma(g.beta, cold[a][b][v], r) : r;
             }
 }
 
@@ -421,23 +430,23 @@ __global__ __launch_bounds__(256) void node128_kernel(double *G, double *C, doub
     auto at = [dp](double *p, int64_t r, int64_t c) { return p + r * dp + c; };
     const int64_t o2 = off + FT;
     int bad = 0;
-    base_block(G, C, X, dp, off, bad);
+    base_block(G, X, dp, off, bad);
     __syncthreads();
     // C21 = G21 X11^T
-    dgemm_tile<FT>(DGemm{at(G, o2, off), dp, at(X, off, off), dp, at(C, o2, off), dp, FT, FT, FT, 0, 2, 0, 1.0, 0.0, 0},
+    dgemm_tile<FT, FT>(DGemm{at(G, o2, off), dp, at(X, off, off), dp, at(C, o2, off), dp, FT, FT, FT, 0, 2, 0, 1.0, 0.0, 0},
                0, 0);
     __syncthreads();
     // G22 -= C21 C21^T
-    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(C, o2, off), dp, at(G, o2, o2), dp, FT, FT, FT, 0, 0, 1, -1.0, 1.0, 0},
+    dgemm_tile<FT, FT>(DGemm{at(C, o2, off), dp, at(C, o2, off), dp, at(G, o2, o2), dp, FT, FT, FT, 0, 0, 1, -1.0, 1.0, 0},
                0, 0);
     __syncthreads();
-    base_block(G, C, X, dp, o2, bad);
+    base_block(G, X, dp, o2, bad);
     __syncthreads();
     // T = C21 X11, X21 = -X22 T
-    dgemm_tile<FT>(DGemm{at(C, o2, off), dp, at(X, off, off), dp, at(T, o2, off), dp, FT, FT, FT, 1, 3, 0, 1.0, 0.0, 0},
+    dgemm_tile<FT, FT>(DGemm{at(C, o2, off), dp, at(X, off, off), dp, at(T, o2, off), dp, FT, FT, FT, 1, 3, 0, 1.0, 0.0, 0},
                0, 0);
     __syncthreads();
-    dgemm_tile<FT>(DGemm{at(X, o2, o2), dp, at(T, o2, off), dp, at(X, o2, off), dp, FT, FT, FT, 1, 1, 0, -1.0, 0.0, 0},
+    dgemm_tile<FT, FT>(DGemm{at(X, o2, o2), dp, at(T, o2, off), dp, at(X, o2, off), dp, FT, FT, FT, 1, 1, 0, -1.0, 0.0, 0},
                0, 0);
     if (bad && dev_status) atomicOr(dev_status, BAKRON_DEV_NOT_PD);
 }
@@ -552,8 +561,8 @@ int32_t take_event(const Factor &fc, hipEvent_t *e) {
 int32_t recurse(const Factor &fc, int64_t off, int64_t n) {
     const int64_t dp = fc.dp;
     if (n == FT) {
-        hipLaunchKernelGGL(base_kernel, dim3(1), dim3(256), 0, fc.stream, fc.f.G, fc.f.C, fc.f.X, dp,
-                           off, fc.dev_status);
+        hipLaunchKernelGGL(base_kernel, dim3(1), dim3(256), 0, fc.stream, fc.f.G, fc.f.X, dp, off,
+                           fc.dev_status);
         BK_LAUNCH_CHECK("base_kernel");
         return BAKRON_OK;
     }
