@@ -207,6 +207,30 @@ __global__ __launch_bounds__(256) void relayout_kernel(
     }
 }
 
+// The leaf's per-column LA band table and per-row 1 / LB_rr, once per solve
+// from the padded factors (the leaf used to build them from its LDS tiles
+// behind a second barrier).  Entry x < np: column x of the grid, in its
+// diagonal block J = x / TB at c = x % TB: LA[x][x - j] for j <= c (j < 8),
+// zero for j > c, and 1 / LA_xx; entry x < mp: 1 / LB_xx.
+__global__ __launch_bounds__(256) void tables_kernel(const float *__restrict__ LAp,
+                                                     const float *__restrict__ LBp, int64_t np,
+                                                     int64_t mp, float4 *tabA, float *tabI, float *ilb) {
+    const int64_t nx = np > mp ? np : mp;
+    for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < nx;
+         x += (int64_t)gridDim.x * blockDim.x) {
+        if (x < np) {
+            const int c = (int)(x % TB);
+            float band[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) band[j] = c >= j ? LAp[x * np + x - j] : 0.0f;
+            tabA[2 * x] = make_float4(band[0], band[1], band[2], band[3]);
+            tabA[2 * x + 1] = make_float4(band[4], band[5], band[6], band[7]);
+            tabI[x] = band[0] != 0.0f ? 1.0f / band[0] : 0.0f;
+        }
+        if (x < mp) ilb[x] = 1.0f / LBp[x * mp + x];
+    }
+}
+
 // --------------------------------------------------------------------- leaf
 struct LeafArgs {
     const float *Wp;  // mp x np working weights (all outside contributions applied)
@@ -223,6 +247,9 @@ struct LeafArgs {
     float *Cd, *Cr;   // contributions of the previous tile diagonal: from the tile above / to the left
     int out_vec;      // ldo % 4 == 0, codes 4-byte and V, E 16-byte aligned: outputs in groups of 4
     int64_t ldo;      // row stride of codes, V and E
+    const float4 *tabA;  // column c of the grid: LA[c][c], LA[c][c-1 .. c-7] within its diagonal block
+    const float *tabI;   // column c: 1 / LA_cc (0 where LA_cc is 0)
+    const float *ilb;    // row r: 1 / LB_rr
 };
 
 
@@ -294,7 +321,6 @@ __device__ __forceinline__ float from_lane_above(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x138, 0xF, 0xF, true));
 }
 
-__device__ __forceinline__ int clamp_col(int c) { return min(max(c, 0), TB - 1); }
 
 // wave 0; lane r = row r.  Every per-step LDS address is linear in the step d:
 // W is stored skewed, the LA tables are padded over every column the lane
@@ -662,6 +688,16 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
         if (push_down) *reinterpret_cast<float4 *>(lf_P + (TB + r) * GP + c4) = l.x2;
     };
     const bool second = tid < TB * 16 - LEAF_THREADS;
+    // the tile's column band table and row reciprocals (kept by threads < TB)
+    const int q = tid & (TB - 1);
+    float4 tb0, tb1;
+    float tbi, ilb;
+    if (tid < TB) {
+        tb0 = a.tabA[2 * (c0 + q)];
+        tb1 = a.tabA[2 * (c0 + q) + 1];
+        tbi = a.tabI[c0 + q];
+        ilb = a.ilb[r0 + q];
+    }
     const PrologueLoads l0 = load_at(tid);
     PrologueLoads l1;
     if (second) l1 = load_at(tid + LEAF_THREADS);
@@ -692,18 +728,20 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
     };
     zero_pad(tid);
     if (second) zero_pad(tid + LEAF_THREADS);
+    // the band table is zero outside the tile's columns
+    for (int x = tid; x < NCX - TB; x += LEAF_THREADS) {
+        const int xx = x < CX ? x : x + TB;
+        lf_Ab[2 * xx] = make_float4(0.f, 0.f, 0.f, 0.f);
+        lf_Ab[2 * xx + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        lf_ila[xx] = 0.0f;
+    }
     store_at(tid, l0);
     if (second) store_at(tid + LEAF_THREADS, l1);
-    __syncthreads();
-    if (tid < TB) lf_row[tid] = make_float4(s_ld, 1.0f / s_ld, z_ld, 1.0f / lf_B[tid * LP + tid]);
-    for (int x = tid; x < NCX; x += LEAF_THREADS) {
-        const int c = x - CX;
-        float band[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) band[j] = (c >= j && c < TB) ? lf_A[c * LP + c - j] : 0.0f;
-        lf_Ab[2 * x] = make_float4(band[0], band[1], band[2], band[3]);
-        lf_Ab[2 * x + 1] = make_float4(band[4], band[5], band[6], band[7]);
-        lf_ila[x] = band[0] != 0.0f ? 1.0f / band[0] : 0.0f;
+    if (tid < TB) {
+        lf_Ab[2 * (CX + q)] = tb0;
+        lf_Ab[2 * (CX + q) + 1] = tb1;
+        lf_ila[CX + q] = tbi;
+        lf_row[tid] = make_float4(s_ld, 1.0f / s_ld, z_ld, ilb);
     }
     __syncthreads();
 
@@ -1554,6 +1592,8 @@ struct Buffers {
     double *partial;
     int *ctr;  // tile counters of the deferred products
     int nctr;
+    float4 *tabA;  // the leaf's LA band table, np x 2 float4 (tables_kernel)
+    float *tabI, *ilb;
 };
 
 // T has one mp x np slab per buffer of the plan (of the whole grid, or of the
@@ -1579,7 +1619,10 @@ size_t carve(void *ws, int64_t mp, int64_t np, Buffers *b) {
     if (N >= 2) nctr = std::max({nctr, shape_info(M, N / 2).side_ops, shape_info(M, N - N / 2).side_ops});
     if (M >= 2) nctr = std::max({nctr, shape_info(M / 2, N).side_ops, shape_info(M - M / 2, N).side_ops});
     int *ctr = cv.take<int>(nctr * SIDE_QUEUES);
-    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part, ctr, nctr * SIDE_QUEUES};
+    float4 *tabA = cv.take<float4>(2 * np);
+    float *tabI = cv.take<float>(np);
+    float *ilb = cv.take<float>(mp);
+    if (b) *b = Buffers{Wp, Eb, Tb, LAp, LBp, sc, zp, Cd, Cr, part, ctr, nctr * SIDE_QUEUES, tabA, tabI, ilb};
     return cv.used;
 }
 
@@ -1719,6 +1762,9 @@ Solve part_view(const Solve &sv, int I0, int J0, int Ms, int Ns) {
     p.b.LBp += r0 * sv.mp + r0;
     p.b.sc += r0;
     p.b.zp += r0;
+    p.b.tabA += 2 * c0;
+    p.b.tabI += c0;
+    p.b.ilb += r0;
     p.b.Ebuf += sv.order == BAKRON_ORDER_LA_FIRST ? r0 * sv.np + c0 : c0 * sv.mp + r0;
     p.codes += r0 * sv.ldo + c0;
     if (p.V) p.V += r0 * sv.ldo + c0;
@@ -1840,6 +1886,9 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LB, m, m, b.LBp,
                        mp, mp, 1, b_vec);
     BK_LAUNCH_CHECK("relayout_kernel");
+    hipLaunchKernelGGL(tables_kernel, dim3((unsigned)((std::max(mp, np) + 255) / 256)), dim3(256), 0,
+                       stream, b.LAp, b.LBp, np, mp, b.tabA, b.tabI, b.ilb);
+    BK_LAUNCH_CHECK("tables_kernel");
     BK_MARK(0);
 
     const auto aligned = [](const void *p, uintptr_t to) {
@@ -1861,7 +1910,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
                             aligned(pv.E, 16);
         LeafArgs la{pb.Wp, pb.Ebuf, pb.LAp, pb.LBp, pb.sc, pb.zp, mp, np, PM, PN, sv.order,
                     sv.qmin, sv.qmax, pv.codes, pv.V, pv.E, pv.m, pv.n, sv.dev_status, pb.Cd, pb.Cr,
-                    out_vec, sv.ldo};
+                    out_vec, sv.ldo, pb.tabA, pb.tabI, pb.ilb};
         const Plan &plan = shape_info(PM, PN).plan;
         hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, stream, b.ctr, b.nctr);
         BK_LAUNCH_CHECK("zero_i32_kernel");
