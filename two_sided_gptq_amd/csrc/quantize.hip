@@ -111,9 +111,9 @@ __device__ void mse_search(const float *row, int64_t n, int kind, int bits, floa
 __global__ __launch_bounds__(256) void qparams_kernel(
     const float *__restrict__ W, int64_t m, int64_t n, int kind, int bits,
     float *__restrict__ scales, float *__restrict__ zeros, float *__restrict__ sc_pad,
-    float *__restrict__ zp_pad, int32_t *dev_status, int mse) {
-    __shared__ float s_amax[256], s_lo[256], s_hi[256];
-    __shared__ int s_bad[256];
+    float *__restrict__ zp_pad, int32_t *dev_status, int mse, int vec) {
+    __shared__ float s_amax[4], s_lo[4], s_hi[4];
+    __shared__ int s_bad[4];
     const int64_t i = blockIdx.x;
     const int t = threadIdx.x;
     float s = 1.0f, z = 0.0f;
@@ -121,27 +121,54 @@ __global__ __launch_bounds__(256) void qparams_kernel(
         float amax = 0.0f, lo = INFINITY, hi = -INFINITY;
         int bad = 0;
         const float *row = W + i * n;
-        for (int64_t j = t; j < n; j += 256) {
-            const float w = row[j];
+        auto take = [&](float w) {
             bad |= !isfinite(w);
             amax = fmaxf(amax, fabsf(w));
             lo = fminf(lo, w);
             hi = fmaxf(hi, w);
-        }
-        s_amax[t] = amax;
-        s_lo[t] = lo;
-        s_hi[t] = hi;
-        s_bad[t] = bad;
-        __syncthreads();
-        for (int off = 128; off > 0; off >>= 1) {
-            if (t < off) {
-                s_amax[t] = fmaxf(s_amax[t], s_amax[t + off]);
-                s_lo[t] = fminf(s_lo[t], s_lo[t + off]);
-                s_hi[t] = fmaxf(s_hi[t], s_hi[t + off]);
-                s_bad[t] |= s_bad[t + off];
+        };
+        if (vec) {  // four float4 loads in flight per thread
+            const float4 *r4 = reinterpret_cast<const float4 *>(row);
+            const int64_t n4 = n / 4;
+            int64_t j = t;
+            for (; j + 3 * 256 < n4; j += 4 * 256) {
+                const float4 a = r4[j], b = r4[j + 256], c = r4[j + 512], d = r4[j + 768];
+                take(a.x); take(a.y); take(a.z); take(a.w);
+                take(b.x); take(b.y); take(b.z); take(b.w);
+                take(c.x); take(c.y); take(c.z); take(c.w);
+                take(d.x); take(d.y); take(d.z); take(d.w);
             }
-            __syncthreads();
+            for (; j < n4; j += 256) {
+                const float4 a = r4[j];
+                take(a.x); take(a.y); take(a.z); take(a.w);
+            }
+        } else {
+            for (int64_t j = t; j < n; j += 256) take(row[j]);
         }
+        // max, min and or are exact in any order: a butterfly in each wave,
+        // then the four waves' values
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            amax = fmaxf(amax, __shfl_xor(amax, off));
+            lo = fminf(lo, __shfl_xor(lo, off));
+            hi = fmaxf(hi, __shfl_xor(hi, off));
+            bad |= __shfl_xor(bad, off);
+        }
+        const int w = t >> 6;
+        if ((t & 63) == 0) {
+            s_amax[w] = amax;
+            s_lo[w] = lo;
+            s_hi[w] = hi;
+            s_bad[w] = bad;
+        }
+        __syncthreads();
+        if (t == 0) {
+            s_amax[0] = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+            s_lo[0] = fminf(fminf(s_lo[0], s_lo[1]), fminf(s_lo[2], s_lo[3]));
+            s_hi[0] = fmaxf(fmaxf(s_hi[0], s_hi[1]), fmaxf(s_hi[2], s_hi[3]));
+            s_bad[0] = s_bad[0] | s_bad[1] | s_bad[2] | s_bad[3];
+        }
+        __syncthreads();
         if (kind == BAKRON_Q_SYM) {
             s = s_amax[0] / (float)((1 << (bits - 1)) - 1);  // IEEE fp32 division
             if (s == 0.0f) s = 1.0f;
@@ -184,13 +211,14 @@ __global__ __launch_bounds__(256) void relayout_kernel(
         const int64_t r = idx / q4;
         const int64_t c0 = (idx - r * q4) * 4;
         float v[4];
-        if (r < rows && vec_ok && c0 + 3 < cols) {
+        const bool read = r < rows && !(tri && c0 > r);  // a factor's strictly upper part is not read
+        if (read && vec_ok && c0 + 3 < cols) {
             const float4 x = *reinterpret_cast<const float4 *>(src + r * cols + c0);
             v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                v[k] = (r < rows && c0 + k < cols) ? src[r * cols + c0 + k] : 0.0f;
+                v[k] = (read && c0 + k < cols) ? src[r * cols + c0 + k] : 0.0f;
         }
         if (tri) {
 #pragma unroll
@@ -1134,7 +1162,18 @@ __global__ __launch_bounds__(256) void sumsq_partial_kernel(const float *__restr
     const int64_t beg = blockIdx.x * chunk;
     const int64_t end = min(count, beg + chunk);
     double s = 0.0;
-    for (int64_t k = beg + threadIdx.x; k < end; k += 256) {
+    int64_t k = beg + threadIdx.x;
+    for (; k + 7 * 256 < end; k += 8 * 256) {  // eight loads in flight; the same order of the sum
+        float xv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xv[u] = x[k + u * 256];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const double v = xv[u];
+            s += v * v;
+        }
+    }
+    for (; k < end; k += 256) {
         const double v = x[k];
         s += v * v;
     }
@@ -1384,14 +1423,20 @@ Plan build_plan(int M, int N, int shift) {
     auto band = [&](const Node &nd, int side, int prod, int lo, int hi) {
         pl.ops.push_back(Op{OP_BAND, side, -1, nd, prod, lo, hi});
     };
+    // A fork's side-stream steps are issued after the next leaf: the dependences
+    // are the same, and a captured graph then creates the leaf's node before the
+    // side branch's.
+    std::vector<Op> forked;
     auto fork = [&](int ev) {
         pl.ops.push_back(Op{OP_RECORD, 0, ev, Node{}, 0, 0, 0});
-        pl.ops.push_back(Op{OP_WAIT, 1, ev, Node{}, 0, 0, 0});
+        forked.push_back(Op{OP_WAIT, 1, ev, Node{}, 0, 0, 0});
     };
     for (const Node &nd : nodes) {
         if (nd.leaf) {
             join(nd.K + 1);
             pl.ops.push_back(Op{OP_LEAF, 0, -1, nd, 0, 0, 0});
+            pl.ops.insert(pl.ops.end(), forked.begin(), forked.end());
+            forked.clear();
             continue;
         }
         const int R = nd.L - nd.H, end = nd.K + nd.L;
@@ -1403,9 +1448,9 @@ Plan build_plan(int M, int N, int shift) {
             join(a);
             band(nd, 0, 1, nd.K + nd.H, a);
             fork(e1);  // after the critical products: the deferred ones run beside the next leaves
-            band(nd, 1, 0, a, end);
-            band(nd, 1, 1, a, end);
-            pl.ops.push_back(Op{OP_RECORD, 1, e3, Node{}, 0, 0, 0});
+            forked.push_back(Op{OP_BAND, 1, -1, nd, 0, a, end});
+            forked.push_back(Op{OP_BAND, 1, -1, nd, 1, a, end});
+            forked.push_back(Op{OP_RECORD, 1, e3, Node{}, 0, 0, 0});
             pending.push_back({a, e3});
         } else {
             band(nd, 0, 0, nd.K, end);
@@ -1413,6 +1458,7 @@ Plan build_plan(int M, int N, int shift) {
             band(nd, 0, 1, nd.K + nd.H, end);
         }
     }
+    pl.ops.insert(pl.ops.end(), forked.begin(), forked.end());
     join(INT_MAX);
     return pl;
 }
@@ -1872,11 +1918,12 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     const Buffers &b = sv.b;
     const int64_t m = sv.m, n = sv.n, mp = sv.mp, np = sv.np;
     BK_MARK(-1);
+    const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.W) & 15) == 0);
     hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, sv.W, m, n,
-                       sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status, sv.mse);
+                       sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status, sv.mse,
+                       w_vec);
     BK_LAUNCH_CHECK("qparams_kernel");
     const unsigned rl_blocks = 256u * 8u;
-    const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.W) & 15) == 0);
     const int a_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LA) & 15) == 0);
     const int b_vec = (m % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LB) & 15) == 0);
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.W, m, n, b.Wp,
@@ -2412,7 +2459,8 @@ extern "C" int32_t bakron_quantize_antidiag(const float *W, int64_t m, int64_t n
     else if (qkind == BAKRON_Q_ASYM) { qmin = 0; qmax = (1 << qbits) - 1; }
     else { qmin = -128; qmax = 127; }
     hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, W, m, n, qkind, qbits,
-                       scales, zeros, sc, zp, dev_status, 0);
+                       scales, zeros, sc, zp, dev_status, 0,
+                       (int)((n % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0)));
     BK_LAUNCH_CHECK("qparams_kernel");
     const unsigned rl_blocks = 256u * 8u;
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, W, m, n, Wp, mp, np, 0, 0);
