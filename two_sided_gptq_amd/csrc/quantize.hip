@@ -1360,7 +1360,7 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
 // leaves in diagonal order and, for every band node, the products that feed
 // its first target diagonals.  A node whose right part spans R = L - H >=
 // SIDE_MIN_R diagonals keeps only the targets K + H .. a - 1, a = K + H +
-// (R >> shift), critical: its first product over the T diagonals from a
+// (R >> shift) (R >> 1 below 2 SIDE_MIN_R), critical: its first product over the T diagonals from a
 // on and its second product over the targets from a on go to the side stream.
 // They are forked by events once their inputs exist (the sources are final
 // when the node starts; the second product also reads the critical part of T)
@@ -1376,6 +1376,10 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
 // same plan gives the same results bit for bit.
 constexpr int OP_LEAF = 0, OP_BAND = 1, OP_RECORD = 2, OP_WAIT = 3;
 constexpr int SIDE_MIN_R = 16;
+// A node with R < 2 SIDE_MIN_R keeps half of its targets critical whatever the
+// shift: a quarter would leave its deferred products only R/4 leaves to run
+// beside, and the critical stream would wait for them (measured at 4096 x 4096:
+// 5.683 -> 5.639 ms with half).
 // The deferred work should fit beside the leaves: the side kernel sustains
 // about 48 TFLOP/s on its CUs and a leaf launch lasts about 25 us, so about
 // 1.2e9 flops per leaf launch.  A shape keeps a quarter of each wide node's
@@ -1440,7 +1444,7 @@ Plan build_plan(int M, int N, int shift) {
             continue;
         }
         const int R = nd.L - nd.H, end = nd.K + nd.L;
-        const int keep = R >= SIDE_MIN_R ? (R >> shift) : R;
+        const int keep = R >= SIDE_MIN_R ? (R >> (R < 2 * SIDE_MIN_R ? 1 : shift)) : R;
         if (keep < R) {
             const int a = nd.K + nd.H + keep;
             const int e1 = pl.events++, e3 = pl.events++;
