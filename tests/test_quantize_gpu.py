@@ -220,6 +220,35 @@ def test_two_stream_modes_agree(bk, m, n, order):
     assert np.max(np.abs(R) / (bound + 1e-30)) <= 1e-4
 
 
+@pytest.mark.parametrize("m,n,order,split", [(1024, 1024, 1, None), (1536, 1024, 2, None),
+                                             (200, 333, 0, None), (520, 780, 0, "rows")])
+def test_workspace_never_read_before_written(bk, m, n, order, split):
+    """A solve reads no workspace byte that it has not written first (the
+    tile counters it clears itself): with every workspace byte set to 0xFF (a
+    NaN in every float, -1 in every counter) the outputs equal, bit for bit,
+    those of a zeroed workspace, and no non-finite value is flagged.  Graph and
+    eager launches, with side launches at the two larger shapes."""
+    print(f"[poison] {m}x{n} order {order} split {split}", flush=True)
+    W, X, Y = synth.custom(m, n, 8100 + m + n)
+    A, B, LA, LB = _factors(X, Y, m)
+    dev = torch.device("cuda:0")
+    Wd, LAd, LBd = (torch.from_numpy(a).to(dev) for a in (W, LA, LB))
+    size = bk.quantize_workspace_size(m, n, 0, 4)
+    runs = []
+    for fill, graph in ((0, True), (255, True), (255, False)):
+        ws = torch.full((size,), fill, dtype=torch.uint8, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = bk.quantize(Wd, LAd, LBd, kind=0, bits=4, order=order, want_E=True, want_sum=True,
+                          dev_status=status, workspace=ws, graph=graph, split=split)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, (fill, graph)
+        runs.append({k: v.cpu().numpy().copy() for k, v in out.items() if v is not None})
+        del ws
+    for r in runs[1:]:
+        for k in runs[0]:
+            assert np.array_equal(r[k].view(np.uint8), runs[0][k].view(np.uint8)), k
+
+
 def _mse_params(W, kind, bits, got_s, got_z):
     """The oracle's MSE-searched parameters, with the GPU's choice accepted on a
     row where it differs only if it is a candidate whose error equals the least

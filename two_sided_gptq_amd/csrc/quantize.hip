@@ -200,7 +200,9 @@ __global__ __launch_bounds__(256) void qparams_kernel(
 // dst (prow x pcol, pcol % 4 == 0) from src (rows x cols).  tri = 0: plain
 // copy with zero padding.  tri = 1: lower triangle of a square factor, upper
 // part zero, padded diagonal one (so padded entries never divide by zero and
-// never couple to real ones).  Each thread writes one float4.
+// never couple to real ones).  tri = 2: as 1, without the 64 x 64 blocks
+// above the diagonal blocks, which the solve's kernels never read.  Each
+// thread writes one float4.
 __global__ __launch_bounds__(256) void relayout_kernel(
     const float *__restrict__ src, int64_t rows, int64_t cols, float *__restrict__ dst,
     int64_t prow, int64_t pcol, int tri, int vec_ok) {
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(256) void relayout_kernel(
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = idx / q4;
         const int64_t c0 = (idx - r * q4) * 4;
+        if (tri == 2 && c0 / TB > r / TB) continue;
         float v[4];
         const bool read = r < rows && !(tri && c0 > r);  // a factor's strictly upper part is not read
         if (read && vec_ok && c0 + 3 < cols) {
@@ -1933,9 +1936,9 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.W, m, n, b.Wp,
                        mp, np, 0, w_vec);
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LA, n, n, b.LAp,
-                       np, np, 1, a_vec);
+                       np, np, 2, a_vec);
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LB, m, m, b.LBp,
-                       mp, mp, 1, b_vec);
+                       mp, mp, 2, b_vec);
     BK_LAUNCH_CHECK("relayout_kernel");
     hipLaunchKernelGGL(tables_kernel, dim3((unsigned)((std::max(mp, np) + 255) / 256)), dim3(256), 0,
                        stream, b.LAp, b.LBp, np, mp, b.tabA, b.tabI, b.ilb);
