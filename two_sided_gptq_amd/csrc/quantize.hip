@@ -108,15 +108,28 @@ __device__ void mse_search(const float *row, int64_t n, int kind, int bits, floa
 // One workgroup per padded row.  Rows >= m get s = 1, z = 0 (the padding is
 // all zeros, so every padded entry rounds to its zero point exactly).  With
 // mse (symmetric and asymmetric kinds) the scale shrink comes from mse_search.
+// With Wp, the workgroup also writes its row of the padded working copy
+// (row stride np, zeros past n; padded rows all zero) as it reads the row.
 __global__ __launch_bounds__(256) void qparams_kernel(
     const float *__restrict__ W, int64_t m, int64_t n, int kind, int bits,
     float *__restrict__ scales, float *__restrict__ zeros, float *__restrict__ sc_pad,
-    float *__restrict__ zp_pad, int32_t *dev_status, int mse, int vec) {
+    float *__restrict__ zp_pad, int32_t *dev_status, int mse, int vec, float *__restrict__ Wp,
+    int64_t np) {
     __shared__ float s_amax[4], s_lo[4], s_hi[4];
     __shared__ int s_bad[4];
     const int64_t i = blockIdx.x;
     const int t = threadIdx.x;
     float s = 1.0f, z = 0.0f;
+    float *wrow = Wp ? Wp + i * np : nullptr;
+    if (wrow) {  // the padding: columns n .. np-1, or the whole of a padded row
+        const int64_t from = i < m ? n : 0;
+        if ((from & 3) == 0) {
+            for (int64_t j = from + 4 * t; j < np; j += 4 * 256)
+                *reinterpret_cast<float4 *>(wrow + j) = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            for (int64_t j = from + t; j < np; j += 256) wrow[j] = 0.0f;
+        }
+    }
     if (i < m) {
         float amax = 0.0f, lo = INFINITY, hi = -INFINITY;
         int bad = 0;
@@ -129,10 +142,17 @@ __global__ __launch_bounds__(256) void qparams_kernel(
         };
         if (vec) {  // four float4 loads in flight per thread
             const float4 *r4 = reinterpret_cast<const float4 *>(row);
+            float4 *w4 = reinterpret_cast<float4 *>(wrow);
             const int64_t n4 = n / 4;
             int64_t j = t;
             for (; j + 3 * 256 < n4; j += 4 * 256) {
                 const float4 a = r4[j], b = r4[j + 256], c = r4[j + 512], d = r4[j + 768];
+                if (w4) {
+                    w4[j] = a;
+                    w4[j + 256] = b;
+                    w4[j + 512] = c;
+                    w4[j + 768] = d;
+                }
                 take(a.x); take(a.y); take(a.z); take(a.w);
                 take(b.x); take(b.y); take(b.z); take(b.w);
                 take(c.x); take(c.y); take(c.z); take(c.w);
@@ -140,10 +160,15 @@ __global__ __launch_bounds__(256) void qparams_kernel(
             }
             for (; j < n4; j += 256) {
                 const float4 a = r4[j];
+                if (w4) w4[j] = a;
                 take(a.x); take(a.y); take(a.z); take(a.w);
             }
         } else {
-            for (int64_t j = t; j < n; j += 256) take(row[j]);
+            for (int64_t j = t; j < n; j += 256) {
+                const float w = row[j];
+                if (wrow) wrow[j] = w;
+                take(w);
+            }
         }
         // max, min and or are exact in any order: a butterfly in each wave,
         // then the four waves' values
@@ -242,10 +267,14 @@ __global__ __launch_bounds__(256) void relayout_kernel(
 // from the padded factors (the leaf used to build them from its LDS tiles
 // behind a second barrier).  Entry x < np: column x of the grid, in its
 // diagonal block J = x / TB at c = x % TB: LA[x][x - j] for j <= c (j < 8),
-// zero for j > c, and 1 / LA_xx; entry x < mp: 1 / LB_xx.
+// zero for j > c, and 1 / LA_xx; entry x < mp: 1 / LB_xx.  Workgroup 0 also
+// clears the nctr tile counters of the deferred band products.
 __global__ __launch_bounds__(256) void tables_kernel(const float *__restrict__ LAp,
                                                      const float *__restrict__ LBp, int64_t np,
-                                                     int64_t mp, float4 *tabA, float *tabI, float *ilb) {
+                                                     int64_t mp, float4 *tabA, float *tabI, float *ilb,
+                                                     int *ctr, int nctr) {
+    if (blockIdx.x == 0)
+        for (int k = threadIdx.x; k < nctr; k += 256) ctr[k] = 0;
     const int64_t nx = np > mp ? np : mp;
     for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < nx;
          x += (int64_t)gridDim.x * blockDim.x) {
@@ -1928,20 +1957,18 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.W) & 15) == 0);
     hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, sv.W, m, n,
                        sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status, sv.mse,
-                       w_vec);
+                       w_vec, b.Wp, np);
     BK_LAUNCH_CHECK("qparams_kernel");
     const unsigned rl_blocks = 256u * 8u;
     const int a_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LA) & 15) == 0);
     const int b_vec = (m % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LB) & 15) == 0);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.W, m, n, b.Wp,
-                       mp, np, 0, w_vec);
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LA, n, n, b.LAp,
                        np, np, 2, a_vec);
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LB, m, m, b.LBp,
                        mp, mp, 2, b_vec);
     BK_LAUNCH_CHECK("relayout_kernel");
     hipLaunchKernelGGL(tables_kernel, dim3((unsigned)((std::max(mp, np) + 255) / 256)), dim3(256), 0,
-                       stream, b.LAp, b.LBp, np, mp, b.tabA, b.tabI, b.ilb);
+                       stream, b.LAp, b.LBp, np, mp, b.tabA, b.tabI, b.ilb, b.ctr, b.nctr);
     BK_LAUNCH_CHECK("tables_kernel");
     BK_MARK(0);
 
@@ -1966,8 +1993,10 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
                     sv.qmin, sv.qmax, pv.codes, pv.V, pv.E, pv.m, pv.n, sv.dev_status, pb.Cd, pb.Cr,
                     out_vec, sv.ldo, pb.tabA, pb.tabI, pb.ilb};
         const Plan &plan = shape_info(PM, PN).plan;
-        hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, stream, b.ctr, b.nctr);
-        BK_LAUNCH_CHECK("zero_i32_kernel");
+        if (k > 0) {  // the first part's counters were cleared by tables_kernel
+            hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, stream, b.ctr, b.nctr);
+            BK_LAUNCH_CHECK("zero_i32_kernel");
+        }
         int side_k = 0;
         for (const Op &op : plan.ops) {
             if (op.kind == OP_RECORD || op.kind == OP_WAIT) {
@@ -2467,7 +2496,8 @@ extern "C" int32_t bakron_quantize_antidiag(const float *W, int64_t m, int64_t n
     else { qmin = -128; qmax = 127; }
     hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, W, m, n, qkind, qbits,
                        scales, zeros, sc, zp, dev_status, 0,
-                       (int)((n % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0)));
+                       (int)((n % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0)), nullptr,
+                       (int64_t)0);
     BK_LAUNCH_CHECK("qparams_kernel");
     const unsigned rl_blocks = 256u * 8u;
     hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, W, m, n, Wp, mp, np, 0, 0);
