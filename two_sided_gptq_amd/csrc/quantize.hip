@@ -105,7 +105,7 @@ __device__ void mse_search(const float *row, int64_t n, int kind, int bits, floa
     z_out = best_z;
 }
 
-// One workgroup per padded row.  Rows >= m get s = 1, z = 0 (the padding is
+// One workgroup per padded row (row0 + block).  Rows >= m get s = 1, z = 0 (the padding is
 // all zeros, so every padded entry rounds to its zero point exactly).  With
 // mse (symmetric and asymmetric kinds) the scale shrink comes from mse_search.
 // With Wp, the workgroup also writes its row of the padded working copy
@@ -114,10 +114,10 @@ __global__ __launch_bounds__(256) void qparams_kernel(
     const float *__restrict__ W, int64_t m, int64_t n, int kind, int bits,
     float *__restrict__ scales, float *__restrict__ zeros, float *__restrict__ sc_pad,
     float *__restrict__ zp_pad, int32_t *dev_status, int mse, int vec, float *__restrict__ Wp,
-    int64_t np) {
+    int64_t np, int64_t row0) {
     __shared__ float s_amax[4], s_lo[4], s_hi[4];
     __shared__ int s_bad[4];
-    const int64_t i = blockIdx.x;
+    const int64_t i = row0 + blockIdx.x;
     const int t = threadIdx.x;
     float s = 1.0f, z = 0.0f;
     float *wrow = Wp ? Wp + i * np : nullptr;
@@ -226,14 +226,14 @@ __global__ __launch_bounds__(256) void qparams_kernel(
 // copy with zero padding.  tri = 1: lower triangle of a square factor, upper
 // part zero, padded diagonal one (so padded entries never divide by zero and
 // never couple to real ones).  tri = 2: as 1, without the 64 x 64 blocks
-// above the diagonal blocks, which the solve's kernels never read.  Each
-// thread writes one float4.
+// above the diagonal blocks, which the solve's kernels never read.  Rows
+// row0 .. row1-1 of dst; each thread writes one float4.
 __global__ __launch_bounds__(256) void relayout_kernel(
     const float *__restrict__ src, int64_t rows, int64_t cols, float *__restrict__ dst,
-    int64_t prow, int64_t pcol, int tri, int vec_ok) {
+    int64_t prow, int64_t pcol, int tri, int vec_ok, int64_t row0, int64_t row1) {
     const int64_t q4 = pcol / 4;
-    const int64_t total = prow * q4;
-    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+    const int64_t total = min(row1, prow) * q4;
+    for (int64_t idx = row0 * q4 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = idx / q4;
         const int64_t c0 = (idx - r * q4) * 4;
@@ -267,18 +267,20 @@ __global__ __launch_bounds__(256) void relayout_kernel(
 // from the padded factors (the leaf used to build them from its LDS tiles
 // behind a second barrier).  Entry x < np: column x of the grid, in its
 // diagonal block J = x / TB at c = x % TB: LA[x][x - j] for j <= c (j < 8),
-// zero for j > c, and 1 / LA_xx; entry x < mp: 1 / LB_xx.  Workgroup 0 also
-// clears the nctr tile counters of the deferred band products.
+// zero for j > c, and 1 / LA_xx; entry x < mp: 1 / LB_xx.  Columns a0 .. a1-1
+// and rows b0 .. b1-1.  Workgroup 0 also clears the nctr tile counters of the
+// deferred band products (nctr = 0: none).
 __global__ __launch_bounds__(256) void tables_kernel(const float *__restrict__ LAp,
                                                      const float *__restrict__ LBp, int64_t np,
                                                      int64_t mp, float4 *tabA, float *tabI, float *ilb,
-                                                     int *ctr, int nctr) {
+                                                     int *ctr, int nctr, int64_t a0, int64_t a1,
+                                                     int64_t b0, int64_t b1) {
     if (blockIdx.x == 0)
         for (int k = threadIdx.x; k < nctr; k += 256) ctr[k] = 0;
-    const int64_t nx = np > mp ? np : mp;
-    for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < nx;
+    const int64_t lo = min(a0, b0), hi = max(min(a1, np), min(b1, mp));
+    for (int64_t x = lo + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < hi;
          x += (int64_t)gridDim.x * blockDim.x) {
-        if (x < np) {
+        if (x >= a0 && x < a1 && x < np) {
             const int c = (int)(x % TB);
             float band[8];
 #pragma unroll
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(256) void tables_kernel(const float *__restrict__ L
             tabA[2 * x + 1] = make_float4(band[4], band[5], band[6], band[7]);
             tabI[x] = band[0] != 0.0f ? 1.0f / band[0] : 0.0f;
         }
-        if (x < mp) ilb[x] = 1.0f / LBp[x * mp + x];
+        if (x >= b0 && x < b1 && x < mp) ilb[x] = 1.0f / LBp[x * mp + x];
     }
 }
 
@@ -1408,6 +1410,7 @@ void band_launches(int order, int K, int L, int H, int M, int N, Launch &p1, Lau
 // same plan gives the same results bit for bit.
 constexpr int OP_LEAF = 0, OP_BAND = 1, OP_RECORD = 2, OP_WAIT = 3;
 constexpr int SIDE_MIN_R = 16;
+constexpr int PREP_TILES = 16;  // tile rows / columns the critical stream sets up itself
 // A node with R < 2 SIDE_MIN_R keeps half of its targets critical whatever the
 // shift: a quarter would leave its deferred products only R/4 leaves to run
 // beside, and the critical stream would wait for them (measured at 4096 x 4096:
@@ -1877,7 +1880,7 @@ int solve_events(const Solve &sv) {
     int part[2][4], ev = 0;
     const int np_ = solve_parts(sv, part);
     for (int k = 0; k < np_; ++k) ev = std::max(ev, shape_info(part[k][2], part[k][3]).plan.events);
-    return ev;
+    return ev + 2;  // and the set-up's fork and join
 }
 
 int32_t launch_band(const Solve &sv, const Op &op, int *ctr, hipStream_t stream, int *launched);
@@ -1954,30 +1957,56 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
     const Buffers &b = sv.b;
     const int64_t m = sv.m, n = sv.n, mp = sv.mp, np = sv.np;
     BK_MARK(-1);
+    // the parts (one without a split) and, between them, the cross update
+    int part[2][4];
+    const int nparts = solve_parts(sv, part);
+    // Set-up: row parameters and W's working copy, the factor copies, the leaf
+    // tables.  With a side stream (one part), the critical stream prepares tile
+    // rows and columns 0 .. PREP_TILES-1 and the side stream the rest, joined
+    // before the first step that reaches past them: a leaf of diagonal >=
+    // PREP_TILES-1 (a pushing leaf reads factor blocks one past its diagonal)
+    // or a band node whose diagonals reach PREP_TILES.
+    const bool split_prep = side && nparts == 1 && sv.M + sv.N - 1 > 2 * PREP_TILES;
+    const int64_t rw = split_prep ? std::min<int64_t>(mp, (int64_t)PREP_TILES * TB) : mp;
+    const int64_t ra = split_prep ? std::min<int64_t>(np, (int64_t)PREP_TILES * TB) : np;
+    const int pe = split_prep ? solve_events(sv) - 2 : -1;
+    if (split_prep) {
+        BK_HIP_CHECK(hipEventRecord((*sync)[pe], stream));
+        BK_HIP_CHECK(hipStreamWaitEvent(side, (*sync)[pe], 0));
+    }
     const int w_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.W) & 15) == 0);
-    hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, sv.W, m, n,
-                       sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status, sv.mse,
-                       w_vec, b.Wp, np);
-    BK_LAUNCH_CHECK("qparams_kernel");
-    const unsigned rl_blocks = 256u * 8u;
     const int a_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LA) & 15) == 0);
     const int b_vec = (m % 4 == 0) && ((reinterpret_cast<uintptr_t>(sv.LB) & 15) == 0);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LA, n, n, b.LAp,
-                       np, np, 2, a_vec);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, sv.LB, m, m, b.LBp,
-                       mp, mp, 2, b_vec);
-    BK_LAUNCH_CHECK("relayout_kernel");
-    hipLaunchKernelGGL(tables_kernel, dim3((unsigned)((std::max(mp, np) + 255) / 256)), dim3(256), 0,
-                       stream, b.LAp, b.LBp, np, mp, b.tabA, b.tabI, b.ilb, b.ctr, b.nctr);
-    BK_LAUNCH_CHECK("tables_kernel");
+    const unsigned rl_blocks = 256u * 8u;
+    auto prep = [&](hipStream_t st, int64_t w0, int64_t w1, int64_t a0, int64_t a1, int clear) {
+        if (w1 > w0)
+            hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)(w1 - w0)), dim3(256), 0, st, sv.W, m, n,
+                               sv.qkind, sv.qbits, sv.scales, sv.zeros, b.sc, b.zp, sv.dev_status,
+                               sv.mse, w_vec, b.Wp, np, w0);
+        if (a1 > a0)
+            hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, st, sv.LA, n, n, b.LAp,
+                               np, np, 2, a_vec, a0, a1);
+        if (w1 > w0)
+            hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, st, sv.LB, m, m, b.LBp,
+                               mp, mp, 2, b_vec, w0, w1);
+        const int64_t span = std::max(a1 - a0, w1 - w0);
+        hipLaunchKernelGGL(tables_kernel, dim3((unsigned)std::max<int64_t>(1, (span + 255) / 256)),
+                           dim3(256), 0, st, b.LAp, b.LBp, np, mp, b.tabA, b.tabI, b.ilb, b.ctr,
+                           clear ? b.nctr : 0, a0, a1, w0, w1);
+    };
+    prep(stream, 0, rw, 0, ra, 1);
+    BK_LAUNCH_CHECK("set-up kernels");
+    if (split_prep) {
+        prep(side, rw, mp, ra, np, 0);
+        BK_LAUNCH_CHECK("set-up kernels (side stream)");
+        BK_HIP_CHECK(hipEventRecord((*sync)[pe + 1], side));
+    }
+    bool prep_joined = !split_prep;
     BK_MARK(0);
 
     const auto aligned = [](const void *p, uintptr_t to) {
         return (reinterpret_cast<uintptr_t>(p) & (to - 1)) == 0;
     };
-    // the parts (one without a split) and, between them, the cross update
-    int part[2][4];
-    const int nparts = solve_parts(sv, part);
     for (int k = 0; k < nparts; ++k) {
         if (k == 1) {
             const int32_t st = cross_update(sv, part[1][0], part[1][1], stream);
@@ -2007,6 +2036,12 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
                 continue;
             }
             const Node &nd = op.nd;
+            const bool crit = op.kind == OP_LEAF || !op.side || !side;
+            if (!prep_joined && crit &&
+                (op.kind == OP_LEAF ? nd.K >= PREP_TILES - 1 : nd.K + nd.L > PREP_TILES)) {
+                BK_HIP_CHECK(hipStreamWaitEvent(stream, (*sync)[pe + 1], 0));
+                prep_joined = true;
+            }
             if (op.kind == OP_LEAF) {
                 const int Ilo = std::max(0, nd.K - PN + 1), Ihi = std::min(PM - 1, nd.K);
                 if (sv.qkind == BAKRON_Q_ASYM)
@@ -2026,6 +2061,7 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
             if (launched) BK_MARK(op.side ? 4 : 2);
         }
     }
+    if (!prep_joined) BK_HIP_CHECK(hipStreamWaitEvent(stream, (*sync)[pe + 1], 0));
     if (sv.sum_e2) {
         hipLaunchKernelGGL(sumsq_partial_kernel, dim3(NPART), dim3(256), 0, stream, b.Ebuf,
                            mp * np, b.partial);
@@ -2497,12 +2533,15 @@ extern "C" int32_t bakron_quantize_antidiag(const float *W, int64_t m, int64_t n
     hipLaunchKernelGGL(qparams_kernel, dim3((unsigned)mp), dim3(256), 0, stream, W, m, n, qkind, qbits,
                        scales, zeros, sc, zp, dev_status, 0,
                        (int)((n % 4 == 0) && ((reinterpret_cast<uintptr_t>(W) & 15) == 0)), nullptr,
-                       (int64_t)0);
+                       (int64_t)0, (int64_t)0);
     BK_LAUNCH_CHECK("qparams_kernel");
     const unsigned rl_blocks = 256u * 8u;
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, W, m, n, Wp, mp, np, 0, 0);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LA, n, n, LAp, np, np, 1, 0);
-    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LB, m, m, LBp, mp, mp, 1, 0);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, W, m, n, Wp, mp, np, 0, 0,
+                       (int64_t)0, mp);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LA, n, n, LAp, np, np, 1, 0,
+                       (int64_t)0, np);
+    hipLaunchKernelGGL(relayout_kernel, dim3(rl_blocks), dim3(256), 0, stream, LB, m, m, LBp, mp, mp, 1, 0,
+                       (int64_t)0, mp);
     BK_LAUNCH_CHECK("relayout_kernel");
     for (int d = 0; d <= (int)(m + n - 2); ++d) {
         const int i_min = (int)std::max<int64_t>(0, d - n + 1), i_max = (int)std::min<int64_t>(m - 1, d);
