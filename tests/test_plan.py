@@ -212,6 +212,39 @@ def test_plan_full_size(lib):
         assert check_plan(m, n, 0) > 0
 
 
+PREP_TILES = 16   # tile rows / columns the critical stream sets up itself
+
+
+@pytest.mark.parametrize("m,n", [(1024, 1024), (4096, 4096), (11008, 4096), (4096, 14336),
+                                 (1000, 3000)])
+def test_setup_join_covers_every_early_step(lib, m, n):
+    """With a side stream the solve's set-up is split: the critical stream
+    prepares tile rows and columns 0 .. PREP_TILES-1 (W and its row parameters,
+    the factor copies, the leaf tables) and joins the side stream's part before
+    the first critical step that is a leaf of diagonal >= PREP_TILES-1 or a band
+    product of a node reaching diagonal PREP_TILES.  Every critical step before
+    that point touches only tiles and factor blocks below PREP_TILES."""
+    M, N = (m + 63) // 64, (n + 63) // 64
+    if M + N - 1 <= 2 * PREP_TILES:
+        pytest.skip("set-up not split")
+    order = int(bakron.schedule_info(m, n, 0)["order"])
+    early = 0
+    for op in bakron.schedule_plan(m, n, order):
+        if op["kind"] == LEAF:
+            if op["K"] >= PREP_TILES - 1:
+                break
+            assert op["K"] + 1 < PREP_TILES   # a pushing leaf reads blocks one past K
+        elif op["kind"] == BAND and op["side"] == 0 and op["rows"] > 0:
+            if op["K"] + op["L"] > PREP_TILES:
+                break
+            for ci, cj, lo, hi in tile_range(op, M, N):
+                assert max(ci, cj, hi) < PREP_TILES, (m, n, op)
+        else:
+            continue
+        early += 1
+    assert early > 0
+
+
 def test_plan_flops_split(lib):
     # deferring moves work between streams but executes the same tiles
     for m, n in [(4096, 4096), (11008, 4096)]:
