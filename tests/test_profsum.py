@@ -93,3 +93,23 @@ def test_summary_without_mfma_pass(tmp_path):
     assert "MFMA work" not in text and "mfma_flops_per_dispatch" not in text
     assert "traffic_bytes_per_dispatch: band_gemm_kernel" in text
 
+
+
+def test_windows_split_setup():
+    """Solves are told apart by their final reductions: a solve with a side
+    stream launches its parameter kernel twice, the second time among its first
+    leaves and band launches."""
+    LEAF = "bakron::(anonymous namespace)::leaf_kernel<false>(bakron::(anonymous namespace)::LeafArgs, int, int)"
+    seq = [BAND,                                   # an earlier call
+           QP, BAND, QP, LEAF, BAND, FIN,          # a graph solve
+           QP, BAND, QP, LEAF, FIN,                # the timed graph solve
+           COPY, QP, LEAF, BAND, FIN,              # the timing pass
+           BAND, BAND]                             # band replays
+    rows, t = [], 0
+    for name in seq:
+        rows.append({"Kernel_Name": name, "Start_Timestamp": str(t), "End_Timestamp": str(t + 10)})
+        t += 20
+    g, tp, rp = profsum._windows(rows)
+    assert [r["Kernel_Name"] for r in g] == [QP, BAND, QP, LEAF, FIN]
+    assert [r["Kernel_Name"] for r in tp] == [QP, LEAF, BAND, FIN]
+    assert [r["Kernel_Name"] for r in rp] == [BAND, BAND]

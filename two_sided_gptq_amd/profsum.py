@@ -52,12 +52,20 @@ def short_name(n: str) -> str:
 
 
 def _windows(rows):
-    """The last timed graph solve (between the last two parameter kernels), the
-    timing pass after it (the same plan in order on one stream, from the last
-    parameter kernel to its final reduction), and the band replays that follow
-    (the critical band launches alone, then the deferred ones), from which the
-    benchmark takes the band kernels' average launch durations."""
+    """The last timed graph solve, the timing pass after it (the same plan in
+    order on one stream), each from its first parameter kernel to its final
+    reduction, and the band replays that follow (the critical band launches
+    alone, then the deferred ones), from which the benchmark takes the band
+    kernels' average launch durations.  A solve with a side stream launches its
+    parameter kernel twice (the first tile rows, then the rest beside the first
+    leaves), so solves are told apart by their final reductions."""
     rows = sorted(rows, key=lambda r: int(r["Start_Timestamp"]))
+    fin = [i for i, r in enumerate(rows) if "sumsq_final_kernel" in r["Kernel_Name"]]
+    if len(fin) >= 2:
+        def start(after):
+            return next(i for i in range(after + 1, len(rows)) if "qparams_kernel" in rows[i]["Kernel_Name"])
+        g0, t0 = start(fin[-3] if len(fin) >= 3 else -1), start(fin[-2])
+        return rows[g0:fin[-2] + 1], rows[t0:fin[-1] + 1], rows[fin[-1] + 1:]
     q = [i for i, r in enumerate(rows) if "qparams_kernel" in r["Kernel_Name"]]
     if len(q) < 2:
         return rows, rows, []
