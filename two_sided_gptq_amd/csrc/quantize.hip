@@ -854,13 +854,23 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_kernel(LeafArgs a, int K, i
                                             ((uint32_t)(uint8_t)(int8_t)(int)q1 << 8) |
                                             ((uint32_t)(uint8_t)(int8_t)(int)q2 << 16) |
                                             ((uint32_t)(uint8_t)(int8_t)(int)q3 << 24);
-                    *reinterpret_cast<uint32_t *>(a.codes + gi * a.ldo + gj) = packed;
+                    // the caller's outputs are not read again here: streaming stores
+                    __builtin_nontemporal_store(packed, reinterpret_cast<uint32_t *>(a.codes + gi * a.ldo + gj));
                     const float4 rc = s_row[r];
-                    if (a.V)
-                        *reinterpret_cast<float4 *>(a.V + gi * a.ldo + gj) =
-                            make_float4(rc.x * (q0 - rc.z), rc.x * (q1 - rc.z), rc.x * (q2 - rc.z),
-                                        rc.x * (q3 - rc.z));
-                    if (a.E) *reinterpret_cast<float4 *>(a.E + gi * a.ldo + gj) = e;
+                    if (a.V) {
+                        float *vp = a.V + gi * a.ldo + gj;
+                        __builtin_nontemporal_store(rc.x * (q0 - rc.z), vp);
+                        __builtin_nontemporal_store(rc.x * (q1 - rc.z), vp + 1);
+                        __builtin_nontemporal_store(rc.x * (q2 - rc.z), vp + 2);
+                        __builtin_nontemporal_store(rc.x * (q3 - rc.z), vp + 3);
+                    }
+                    if (a.E) {
+                        float *ep = a.E + gi * a.ldo + gj;
+                        __builtin_nontemporal_store(e.x, ep);
+                        __builtin_nontemporal_store(e.y, ep + 1);
+                        __builtin_nontemporal_store(e.z, ep + 2);
+                        __builtin_nontemporal_store(e.w, ep + 3);
+                    }
                 }
             }
         } else {
