@@ -947,8 +947,8 @@ __device__ inline bool band_tile(const BandArgs &g, int bx, int by, int &ci, int
 // its A quadrant and row l%32 of its B quadrant; the two k slots of each
 // instruction are k and k+32 of the 64-wide block (lanes 0-31 take the lower
 // half, lanes 32-63 the upper), so every lane reads its operands as
-// contiguous float4 from LDS.  The next K block is prefetched into registers
-// while the current one is multiplied.
+// contiguous float4 from LDS.  The K block after next is prefetched into
+// registers while the current one is multiplied (two register sets).
 __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
     // Workgroups go to the 8 XCDs round-robin by linear id; XCD x takes the
     // rows y = x (mod 8), a whole row at a time, so the operand block that a
@@ -971,21 +971,49 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
     const float *Ab = g.A + (int64_t)ci * TB * g.lda + (int64_t)lr * g.lda + lc;
     const float *Bb = g.B + (int64_t)cj * TB * g.ldb + (int64_t)lr * g.ldb + lc;
     const int64_t sa = 16 * g.lda, sb = 16 * g.ldb;
+    // two register sets, each holding one K block's operands: block kb + 2 is
+    // fetched while block kb is multiplied, so a load has two blocks' MFMA time
+    // to arrive.  Past the last block the loads repeat it (always in bounds),
+    // so every iteration issues the same loads and the waits stay static.
     float4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define BK_GLOAD(kb)                                                                 \
+    float4 xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3;
+#define BK_GLOAD(kb, A0, A1, A2, A3, B0, B1, B2, B3)                                 \
     do {                                                                             \
         const float *a_ = Ab + (kb) * TB;                                            \
         const float *b_ = Bb + (kb) * TB;                                            \
-        ra0 = *reinterpret_cast<const float4 *>(a_);                                 \
-        ra1 = *reinterpret_cast<const float4 *>(a_ + sa);                            \
-        ra2 = *reinterpret_cast<const float4 *>(a_ + 2 * sa);                        \
-        ra3 = *reinterpret_cast<const float4 *>(a_ + 3 * sa);                        \
-        rb0 = *reinterpret_cast<const float4 *>(b_);                                 \
-        rb1 = *reinterpret_cast<const float4 *>(b_ + sb);                            \
-        rb2 = *reinterpret_cast<const float4 *>(b_ + 2 * sb);                        \
-        rb3 = *reinterpret_cast<const float4 *>(b_ + 3 * sb);                        \
+        A0 = *reinterpret_cast<const float4 *>(a_);                                  \
+        A1 = *reinterpret_cast<const float4 *>(a_ + sa);                             \
+        A2 = *reinterpret_cast<const float4 *>(a_ + 2 * sa);                         \
+        A3 = *reinterpret_cast<const float4 *>(a_ + 3 * sa);                         \
+        B0 = *reinterpret_cast<const float4 *>(b_);                                  \
+        B1 = *reinterpret_cast<const float4 *>(b_ + sb);                             \
+        B2 = *reinterpret_cast<const float4 *>(b_ + 2 * sb);                         \
+        B3 = *reinterpret_cast<const float4 *>(b_ + 3 * sb);                         \
     } while (0)
-    BK_GLOAD(klo);
+#define BK_LSTORE(A0, A1, A2, A3, B0, B1, B2, B3)                                    \
+    do {                                                                             \
+        *reinterpret_cast<float4 *>(as_w) = A0;                                      \
+        *reinterpret_cast<float4 *>(as_w + 16 * GP) = A1;                            \
+        *reinterpret_cast<float4 *>(as_w + 32 * GP) = A2;                            \
+        *reinterpret_cast<float4 *>(as_w + 48 * GP) = A3;                            \
+        *reinterpret_cast<float4 *>(bs_w) = B0;                                      \
+        *reinterpret_cast<float4 *>(bs_w + 16 * GP) = B1;                            \
+        *reinterpret_cast<float4 *>(bs_w + 32 * GP) = B2;                            \
+        *reinterpret_cast<float4 *>(bs_w + 48 * GP) = B3;                            \
+    } while (0)
+#define BK_MFMA()                                                                    \
+    do {                                                                             \
+        _Pragma("unroll") for (int s4 = 0; s4 < 8; ++s4) {                           \
+            const float4 av = *reinterpret_cast<const float4 *>(ap + 4 * s4);        \
+            const float4 bv = *reinterpret_cast<const float4 *>(bp + 4 * s4);        \
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);    \
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);    \
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);    \
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);    \
+        }                                                                            \
+    } while (0)
+    BK_GLOAD(klo, ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3);
+    BK_GLOAD(min(klo + 1, khi), xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3);
     // accumulator layout of the 32 x 32 MFMA: lane l holds column l % 32;
     // register v holds row 8 (v / 4) + 4 (l / 32) + v % 4.  The old values of
     // a subtracted tile are loaded now, so their latency overlaps the K loop.
@@ -1003,29 +1031,23 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
     const float *bp = Bs + (wc * 32 + (lane & 31)) * GP + 32 * (lane >> 5);
     float *as_w = As + lr * GP + lc;
     float *bs_w = Bs + lr * GP + lc;
-    for (int kb = klo; kb <= khi; ++kb) {
+    for (int kb = klo;; kb += 2) {
         __syncthreads();
-        *reinterpret_cast<float4 *>(as_w) = ra0;
-        *reinterpret_cast<float4 *>(as_w + 16 * GP) = ra1;
-        *reinterpret_cast<float4 *>(as_w + 32 * GP) = ra2;
-        *reinterpret_cast<float4 *>(as_w + 48 * GP) = ra3;
-        *reinterpret_cast<float4 *>(bs_w) = rb0;
-        *reinterpret_cast<float4 *>(bs_w + 16 * GP) = rb1;
-        *reinterpret_cast<float4 *>(bs_w + 32 * GP) = rb2;
-        *reinterpret_cast<float4 *>(bs_w + 48 * GP) = rb3;
+        BK_LSTORE(ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3);
         __syncthreads();
-        if (kb < khi) BK_GLOAD(kb + 1);
-#pragma unroll
-        for (int s4 = 0; s4 < 8; ++s4) {
-            const float4 av = *reinterpret_cast<const float4 *>(ap + 4 * s4);
-            const float4 bv = *reinterpret_cast<const float4 *>(bp + 4 * s4);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc, 0, 0, 0);
-        }
+        BK_GLOAD(min(kb + 2, khi), ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3);
+        BK_MFMA();
+        if (kb + 1 > khi) break;
+        __syncthreads();
+        BK_LSTORE(xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3);
+        __syncthreads();
+        BK_GLOAD(min(kb + 3, khi), xa0, xa1, xa2, xa3, xb0, xb1, xb2, xb3);
+        BK_MFMA();
+        if (kb + 2 > khi) break;
     }
 #undef BK_GLOAD
+#undef BK_LSTORE
+#undef BK_MFMA
     if (g.subtract) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) cb[(int64_t)(8 * (v >> 2) + (v & 3)) * g.ldc] = old[v] - acc[v];
