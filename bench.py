@@ -16,6 +16,9 @@ Prints one JSON line.  Besides the contract fields it carries
                 same duration).  The leaf kernel takes about as long in total
                 (dominant_kernel names the longer phase) but is bound by its
                 chain of dependent steps, not by a throughput roofline
+  gemm_phase    the whole band phase (critical and deferred products): useful
+                flops over the kernel time of the two band replays, against the
+                fp32 MFMA peak
   leaf          the leaf phase: HBM bytes per launch, launches, in-kernel steps,
                 and its in-tile flops against the fp32 vector peak
   prep          bakron_hessian and bakron_factor for both Kronecker factors,
@@ -229,6 +232,14 @@ def main():
                 "launches": band_launches, "counted_mfma_flops_per_launch": counted,
                 "mfma_util_counted": mfma_util}
 
+    phase_ms = ph["band_replay_ms"] + ph["side_replay_ms"]
+    # null for a single tile diagonal, which has no band product
+    phase_tflops = (sched["useful_band_flops"] / (phase_ms / 1e3) / 1e12
+                    if band_launches and phase_ms > 0 else None)
+    gemm_phase = {"useful_flops": sched["useful_band_flops"],
+                  "critical_replay_ms": ph["band_replay_ms"], "deferred_replay_ms": ph["side_replay_ms"],
+                  "tflops": phase_tflops,
+                  "frac": phase_tflops / FP32_MFMA_PEAK_TFLOPS if phase_tflops else None}
     result = {
         "metric": "weight entries quantized/sec at 4096x4096 INT4; % of fp32 MFMA peak",
         "value": value, "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
@@ -248,6 +259,10 @@ def main():
         # order on one stream; the timed graph overlaps the deferred products
         # (side_ms) with the leaves, so the phases add up to more than ms_per_step
         "phases_ms": {k: ph[k] for k in ("prep_ms", "leaf_ms", "band_ms", "side_ms", "final_ms")},
+        # the whole band phase: every band product's useful flops (critical and
+        # deferred) over the two replays' kernel time (critical launches back to
+        # back, then the deferred launches alone on their capped CU share)
+        "gemm_phase": gemm_phase,
         "side": {"kernel": "band_side_kernel", "launches": int(sched["side_launches"]),
                  "useful_flops": sched["side_useful_flops"],
                  "replay_ms": ph["side_replay_ms"], "tflops_alone": side_tflops},

@@ -46,6 +46,12 @@ def test_report_fields():
     assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 157.3
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
     assert 0 < rf["frac"] < 1
+    # the whole band phase: critical and deferred useful flops over both replays
+    gp = r["gemm_phase"]
+    assert gp["useful_flops"] == r["schedule"]["useful_band_flops"]
+    ms = gp["critical_replay_ms"] + gp["deferred_replay_ms"]
+    assert abs(gp["tflops"] - gp["useful_flops"] / (ms / 1e3) / 1e12) < 1e-6 * gp["tflops"]
+    assert 0 < gp["frac"] < 1
     # the leaf's algorithmic bytes: W in, E, codes, V out, and the lower
     # triangles of the two diagonal factor blocks of each 64 x 64 tile
     assert r["leaf"]["alg_bytes"] == r["config"]["m"] * r["config"]["n"] * (13 + 8 * 2080 / 4096)
@@ -69,4 +75,5 @@ def test_report_single_tile_workload():
     assert r["value"] > 0 and r["config"]["m"] == 64
     assert r["roofline"]["achieved"] is None and r["roofline"]["frac"] is None
     assert r["roofline"]["traffic"] is None
+    assert r["gemm_phase"]["tflops"] is None and r["gemm_phase"]["frac"] is None
     assert r["leaf"]["launches"] == 1
