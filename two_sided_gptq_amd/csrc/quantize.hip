@@ -955,12 +955,20 @@ __global__ __launch_bounds__(256) void band_gemm_kernel(BandArgs g) {
     // row shares (its A rows) is fetched into one XCD's L2 only.  Longest
     // tiles first: the K depth grows with the band offset in every mode and
     // with the row in the second products, so those run backwards.
-    const int lin = blockIdx.y * gridDim.x + blockIdx.x, slot = lin >> 3;
-    const int gy = (lin & 7) + 8 * (slot / (int)gridDim.x);
-    const int gx = slot % (int)gridDim.x;
-    if (gy >= g.rows) return;
+    // The second products read, update and write back W tiles: there XCD x
+    // takes the output tile rows I' = x (mod 8) in every launch, so the next
+    // launch that updates a tile row runs on the XCD that holds it.
+    const int lin = blockIdx.y * gridDim.x + blockIdx.x, slot = lin >> 3, x = lin & 7;
+    const int gx = slot % (int)gridDim.x, k = slot / (int)gridDim.x;
+    int by;
+    if (g.mode == 1 || g.mode == 3) {
+        by = g.rows - 1 - (((g.rlo + g.rows - 1 - x) % 8 + 8) % 8) - 8 * k;
+        if (by < 0) return;
+    } else {
+        by = x + 8 * k;
+        if (by >= g.rows) return;
+    }
     const int bx = g.olo + gridDim.x - 1 - gx;
-    const int by = (g.mode == 1 || g.mode == 3) ? g.rows - 1 - gy : gy;
     int ci, cj, klo, khi;
     if (!band_tile(g, bx, by, ci, cj, klo, khi)) return;
     __shared__ __align__(16) float As[TB * GP];
@@ -2076,11 +2084,12 @@ int32_t enqueue_solve(const Solve &sv, hipStream_t stream, hipStream_t side,
             }
             if (op.kind == OP_LEAF) {
                 const int Ilo = std::max(0, nd.K - PN + 1), Ihi = std::min(PM - 1, nd.K);
+                const unsigned nwg = (unsigned)(Ihi - Ilo + 1);
                 if (sv.qkind == BAKRON_Q_ASYM)
-                    hipLaunchKernelGGL(leaf_kernel<true>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0,
+                    hipLaunchKernelGGL(leaf_kernel<true>, dim3(nwg), dim3(LEAF_THREADS), 0,
                                        stream, la, nd.K, nd.flags);
                 else
-                    hipLaunchKernelGGL(leaf_kernel<false>, dim3(Ihi - Ilo + 1), dim3(LEAF_THREADS), 0,
+                    hipLaunchKernelGGL(leaf_kernel<false>, dim3(nwg), dim3(LEAF_THREADS), 0,
                                        stream, la, nd.K, nd.flags);
                 BK_LAUNCH_CHECK("leaf_kernel");
                 BK_MARK(1);
